@@ -1,0 +1,104 @@
+"""Test-side helpers: small hand-built layers and the margin filter."""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from sparse_moe_layer_fwd_amd.workloads import MoEConfig
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+class ArrayLayer:
+    """A layer whose stored tensors are given as arrays (for pins and invariances)."""
+
+    def __init__(self, cfg: MoEConfig, x, w_router, w1, w2, w_down=None, w_up=None,
+                 b_router=None, ws1=None, ws2=None):
+        self.cfg = cfg
+        self._x, self._wr, self._w1, self._w2 = x, w_router, w1, w2
+        self._wd, self._wu, self._br, self._ws1, self._ws2 = w_down, w_up, b_router, ws1, ws2
+
+    def x(self):
+        return self._x
+
+    def w_down(self):
+        return self._wd
+
+    def w_up(self):
+        return self._wu
+
+    def w_router(self):
+        return self._wr
+
+    def b_router(self):
+        return self._br
+
+    def w1(self, e):
+        return self._w1[e]
+
+    def w2(self, e):
+        return self._w2[e]
+
+    def ws1(self):
+        return self._ws1
+
+    def ws2(self):
+        return self._ws2
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f64_layer(cfg: MoEConfig, rng: np.random.Generator, T=None):
+    """Random float64 layer of shape ``cfg`` (act/expert dtype 'f64'), for pins."""
+    T = cfg.T if T is None else T
+    d, l, N, m = cfg.d, cfg.latent, cfg.n_experts, cfg.ffn
+    c = cfg.replace(act="f64", expert="f64", T=T)
+    x = rng.standard_normal((T, d))
+    wd = rng.standard_normal((l, d)) / np.sqrt(d) if cfg.has_latent_proj else None
+    wu = rng.standard_normal((d, l)) / np.sqrt(l) if cfg.has_latent_proj else None
+    wr = rng.standard_normal((N, l)) / np.sqrt(l)
+    w1 = rng.standard_normal((N, m, l)) / np.sqrt(l)
+    w2 = rng.standard_normal((N, l, m)) / np.sqrt(m)
+    ws1 = ws2 = None
+    if cfg.n_shared:
+        ws1 = rng.standard_normal((cfg.n_shared, cfg.shared_ffn, d)) / np.sqrt(d)
+        ws2 = rng.standard_normal((cfg.n_shared, d, cfg.shared_ffn)) / np.sqrt(cfg.shared_ffn)
+    return c, ArrayLayer(c, x, wr, w1, w2, wd, wu, None, ws1, ws2)
+
+
+def margin_filter(wl, cfg, max_rounds=20):
+    """Redraw tokens whose fp64 top-K gap is below cfg.margin (the configs ask for
+    routing inputs without near-ties).  Uses the oracle's routing; returns the
+    number of rows redrawn.  The redraws come from the generator's per-(token,
+    attempt) streams, so the result is reproducible."""
+    import oracle
+    if cfg.top_k >= cfg.n_experts:
+        return 0
+    x = np.array(wl.x(), copy=True)
+    wd = wl.w_down()
+    wd64 = None if wd is None else oracle.decode_expert(wd, cfg.act)
+    wr, br = wl.w_router(), wl.b_router()
+    redrawn = 0
+    attempt = np.zeros(cfg.T, dtype=np.int64)
+    bad = np.arange(cfg.T)
+    for _ in range(max_rounds):
+        z = oracle.latent_down(oracle.decode_expert(x[bad], cfg.act), wd64)
+        lg = oracle.router_logits(z, wr, br)
+        srt = -np.sort(-lg, axis=1)
+        gap = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k]
+        bad = bad[gap < cfg.margin]
+        if bad.size == 0:
+            break
+        for t in bad:
+            attempt[t] += 1
+            x[t] = wl.x_redraw(int(t), int(attempt[t]))
+            redrawn += 1
+    else:
+        raise RuntimeError("margin filter did not converge")
+    wl.set_x(x)
+    return redrawn
