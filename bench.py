@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""LatentMoE layer forward throughput on one MI355X.
+
+One step = one moe_forward over a batch of T tokens: down-projection, fp32
+router, top-K/softmax, expert histogram/scan/scatter, the two grouped expert
+GEMMs, combine and up-projection, all in libmoe.so on HBM-resident inputs.
+
+    python bench.py [--config 3] [--steps 20] [--warmup 5] [--gpus 1]
+
+Prints one JSON line.  `value` is tokens/s of the whole layer.  `roofline`
+describes the dominant kernel (the grouped expert GEMMs): its algorithmic
+FLOPs or bytes per launch over its average launch duration, measured with HIP
+events on the launch stream during the timed region (the library's stage
+timer).  `cpu_baseline` is the plain fp64 CPU oracle timed on a bounded sample
+of the same workload (rank 0, N = 1 only).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LatentMoE layer tokens/sec on 1 MI355X; % MFMA peak (prefill), % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+CPU_SAMPLE = {1: 64, 2: 256, 3: 512, 4: 64, 5: 96}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def expert_weight_bytes_per_matrix(cfg):
+    el = cfg.latent * cfg.ffn
+    if cfg.expert == "nvfp4":
+        return el / 2 + el / 16 + 4
+    return el * (4 if cfg.expert == "f32" else 2)
+
+
+def cpu_baseline(cfg, seed, sample):
+    """Time the fp64 oracle on the first `sample` tokens of the same workload."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from sparse_moe_layer_fwd_amd.workloads import Workload
+    sub = cfg.replace(T=sample)
+    wl = Workload(sub, seed)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.forward(wl, sub)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "first %d of the %d tokens of the same workload (seed %d), whole layer in "
+                      "fp64 numpy incl. per-expert weight decode; %.2f s" % (sample, cfg.T, seed, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-5 (default 3)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build measures the layer on a single MI355X "
+              "(--gpus %d requested). Multi-GPU expert parallelism is not built." % args.gpus,
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_fwd_amd import binding as B
+    from sparse_moe_layer_fwd_amd.layer import DeviceLayer, x_to_device
+    from sparse_moe_layer_fwd_amd.workloads import CONFIGS, Workload
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log("bench: config %d %s, generating weights" % (args.config, cfg.name))
+    t0 = time.perf_counter()
+    wl = Workload(cfg, args.seed)
+    layer = DeviceLayer.from_workload(wl, device=dev, threads=16)
+    x = x_to_device(wl, dev)
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.act_torch_dtype(), device=dev)
+    ws = layer.new_workspace(cfg.T)
+    torch.cuda.synchronize()
+    log("bench: inputs resident in HBM (%.1f s); warmup %d" % (time.perf_counter() - t0, args.warmup))
+
+    for _ in range(args.warmup):
+        layer.forward(x, ws=ws, y=y)
+    y2, idx, gate, counts = layer.forward(x, ws=ws, y=y, routing=True)
+    torch.cuda.synchronize()
+    counts_np = counts.cpu().numpy()
+    touched = int((counts_np > 0).sum())
+
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.moe_profile_read()                      # clear
+    B.moe_profile_enable(True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        layer.forward(x, ws=ws, y=y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    B.moe_profile_enable(False)
+    stages = B.moe_profile_read()
+    ms_step = start.elapsed_time(end) / args.steps
+    log("bench: %.3f ms/step" % ms_step)
+
+    # dominant kernel: the grouped expert GEMMs (two launches per step)
+    n_up, ms_up = stages["expert_up"]
+    n_dn, ms_dn = stages["expert_down"]
+    launches = n_up + n_dn
+    avg_ms = (ms_up + ms_dn) / max(1, launches)
+    flops_launch = 2.0 * cfg.T * cfg.top_k * cfg.latent * cfg.ffn
+    wbytes = touched * expert_weight_bytes_per_matrix(cfg)
+    act_es = 4 if cfg.act == "f32" else 2
+    act_bytes = cfg.T * cfg.top_k * (cfg.latent + cfg.ffn) * act_es   # rows in + rows out
+    bytes_launch = wbytes + act_bytes
+    peak_f = PEAK_F32_TFLOPS if cfg.expert == "f32" else PEAK_BF16_TFLOPS
+    t_mfma = flops_launch / (peak_f * 1e12)
+    t_hbm = bytes_launch / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_mfma:
+        ach = bytes_launch / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        ach = flops_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4), "traffic": None}
+    roof.update({"kernel": "grouped expert GEMM (%s)" % ("skinny_kernel" if cfg.T <= 64 and cfg.act != "f32"
+                                                         else "gemm_bf16_kernel" if cfg.act != "f32"
+                                                         else "gemm_f32_kernel"),
+                 "launches": launches, "avg_launch_ms": round(avg_ms, 5),
+                 "algorithmic_flops_per_launch": flops_launch,
+                 "algorithmic_bytes_per_launch": bytes_launch})
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4-weights/bf16" if cfg.expert == "nvfp4" else cfg.act,
+        "data": "synthetic (seeded random weights and inputs, shapes of the layer configuration)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "latent": cfg.latent,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "ffn": cfg.ffn,
+                   "n_shared": cfg.n_shared, "expert_dtype": cfg.expert,
+                   "zipf_s": cfg.zipf_s, "experts_touched": touched,
+                   "max_rows_per_expert": int(counts_np.max()), "parallelism": "single GPU"},
+        "layer_tflops": round(cfg.flops() / (ms_step * 1e-3) / 1e12, 2),
+        "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in stages.items() if v[0]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or CPU_SAMPLE.get(args.config, 64)
+        log("bench: CPU oracle baseline on %d tokens" % sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.seed, sample)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * moe.h - C ABI of the MI355X LatentMoE layer forward library (libmoe.so).
+ *
+ * The layer (sources cited by page title and section):
+ *   - LatentMoE: each token is projected from the hidden size d to a latent
+ *     size l < d (d/l about 4), routed to K of N experts whose FFNs run in the
+ *     latent space, combined, and projected back to d.  Per-expert weight
+ *     traffic and routed payload shrink by d/l.  ("NVIDIA Nemotron 3: Efficient
+ *     and Open Intelligence" Korean summary, section 2.2 LatentMoE; notes.yuuk.io
+ *     Nemotron 3 note, method 2 LatentMoE.)
+ *   - Standard MoE with always-on shared experts (l = d, no projection):
+ *     Nemotron 3 Nano blog, granular MoE section (128 experts, 6 active, 2 shared).
+ *   - NVFP4 expert weights: E2M1 elements, one E4M3 scale per 16-element block,
+ *     one FP32 global scale (Korean summary, section 2.4 NVFP4 Training); the
+ *     Ultra release ships NVFP4 routed experts (Ultra release news, quantization).
+ * Readings taken where the pages are silent: the router is one linear layer
+ * (fp32, optional bias) on the latent; gates are the softmax over the K selected
+ * logits; the expert FFN is W2 * sqrelu(W1 * z) with sqrelu(h) = max(h,0)^2 and
+ * no biases; equal logits select the lower expert id; routing is dropless.
+ *
+ * Conventions
+ *   - Row-major everywhere; weights are [out][in] (reduction dim contiguous).
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, 16-byte
+ *     aligned.  The library never allocates or frees device memory.  Weights
+ *     must outlive the handle.
+ *   - Work is enqueued on the caller's HIP stream (a hipStream_t passed as
+ *     void*, NULL = the null stream).  Calls return right after enqueueing; no
+ *     call synchronises the host.  Faults during execution surface at the
+ *     caller's next synchronisation, as the HIP runtime reports them.
+ *   - Errors are integer status codes; every argument check runs on the host
+ *     before any launch, so a failing call enqueues nothing.
+ *   - A handle is immutable after moe_init and may be used from several host
+ *     threads; concurrent calls need distinct workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_handle* moe_handle_t;
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, K > N, T > max_tokens, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented shape / dtype combination */
+  MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_size() */
+  MOE_ERR_NO_DEVICE = 4,     /* no HIP device visible */
+  MOE_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2 };
+
+typedef struct {
+  int32_t d;               /* hidden size                                   */
+  int32_t latent;          /* latent size l (== d when has_latent_proj = 0) */
+  int32_t n_experts;       /* N routed experts, 1..1024                     */
+  int32_t top_k;           /* K active experts per token, 1..min(N, 64)     */
+  int32_t ffn;             /* m, routed expert FFN width                    */
+  int32_t n_shared;        /* S always-on shared experts (at d), may be 0   */
+  int32_t shared_ffn;      /* shared expert FFN width                       */
+  int32_t max_tokens;      /* largest T any call will pass                  */
+  int32_t has_latent_proj; /* 1: LatentMoE; 0: standard MoE, latent == d    */
+  int32_t act_dtype;       /* MOE_F32 or MOE_BF16: x, projections, y        */
+  int32_t expert_dtype;    /* MOE_F32 (with act F32), MOE_BF16 or MOE_NVFP4 */
+} moe_config_t;
+
+typedef struct {
+  const void* w_down;      /* [l][d] act dtype; NULL unless has_latent_proj          */
+  const float* w_router;   /* [N][l] fp32                                            */
+  const float* b_router;   /* [N] fp32 added to the logits before top-K, or NULL     */
+  const void* w1;          /* [N][m][l]; NVFP4: packed codes uint8 [N][m][l/2]       */
+  const void* w2;          /* [N][l][m]; NVFP4: packed codes uint8 [N][l][m/2]       */
+  const uint8_t* w1_scale; /* NVFP4 only: E4M3 bytes [N][m][l/16], else NULL          */
+  const uint8_t* w2_scale; /* NVFP4 only: E4M3 bytes [N][l][m/16], else NULL          */
+  const float* w1_gscale;  /* NVFP4 only: [N] fp32 global scales, else NULL           */
+  const float* w2_gscale;  /* NVFP4 only: [N] fp32 global scales, else NULL           */
+  const void* w_up;        /* [d][l] act dtype; NULL unless has_latent_proj          */
+  const void* ws1;         /* [S][shared_ffn][d] act dtype, NULL if S == 0           */
+  const void* ws2;         /* [S][d][shared_ffn] act dtype, NULL if S == 0           */
+} moe_weights_t;
+/* NVFP4 packing: element 2j of a row in the low nibble of byte j, element 2j+1
+ * in the high nibble; block b of a row covers elements 16b..16b+15 along the
+ * reduction dimension; w = e2m1(code) * e4m3(scale) * gscale[expert]. */
+
+/* Create a handle for one layer.  Host only: validates the configuration and
+ * weight pointers, binds the caller-owned weights, reads the current device's
+ * compute-unit count.  No device work.
+ * Shape rules: d, l, m, shared_ffn multiples of 64; N <= 1024; K <= min(N, 64);
+ * act F32 requires expert F32; act BF16 requires expert BF16 or NVFP4.
+ * Returns MOE_ERR_NO_DEVICE when no HIP device is visible. */
+int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out);
+
+/* Bytes of device workspace a call with T tokens needs (T <= max_tokens). */
+int moe_workspace_size(moe_handle_t h, int32_t T, size_t* bytes);
+
+/* Routing only: down-projection (if latent), router GEMV, top-K + softmax and
+ * the per-expert histogram.  Writes idx [T][K] int32 (per token in descending
+ * logit order, equal logits -> lower id), gate [T][K] fp32 (softmax over the
+ * K selected logits, gate[t][k] pairs with idx[t][k]) and counts [N] int32.
+ * x is [T][d] in the act dtype.  T == 0 returns MOE_OK and enqueues nothing. */
+int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gate,
+              int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: y [T][d] (act dtype) = LatentMoE(x).  idx/gate/counts are
+ * optional outputs (each may be NULL) with the same meaning and exactly the
+ * same values as moe_route's.  Deterministic: the same inputs give bitwise
+ * the same outputs (no floating-point atomics; fixed summation orders). */
+int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
+                int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Release a handle (host memory only).  NULL is accepted. */
+int moe_destroy(moe_handle_t h);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* ---- stage timing (benchmarks; off by default) ----
+ * Stages of one call, in launch order.  EXPERT_UP and EXPERT_DOWN are the two
+ * grouped expert GEMMs; SHARED covers both shared-expert GEMMs. */
+enum moe_stage {
+  MOE_STAGE_DOWN_PROJ = 0, MOE_STAGE_ROUTER, MOE_STAGE_TOPK, MOE_STAGE_SCAN,
+  MOE_STAGE_SCATTER, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_SHARED,
+  MOE_STAGE_COMBINE, MOE_STAGE_UP_PROJ, MOE_NUM_STAGES
+};
+
+/* enable = 1: later moe_route / moe_forward calls record a HIP event pair
+ * around each stage on the caller's stream (process-wide setting; the events
+ * are host-side objects, no device memory is allocated).  enable = 0 stops
+ * recording.  Returns MOE_OK, or MOE_ERR_HIP if an event cannot be created. */
+int moe_profile_enable(int enable);
+
+/* Waits for every recorded event, then writes per stage the number of
+ * recorded launches (launches[MOE_NUM_STAGES]) and their summed durations in
+ * milliseconds (ms[MOE_NUM_STAGES]), and clears the record.  Either pointer
+ * may be NULL. */
+int moe_profile_read(int32_t* launches, double* ms);
+
+/* Static name of a stage ("expert_up", ...), or "unknown". */
+const char* moe_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,132 @@
+"""ctypes binding of libmoe.so: the same six entry points as include/moe.h.
+
+Argument marshalling only; every step of the layer runs in the HIP library.
+Importing this module does not load the library; ``lib()`` does, and raises
+if it has not been built (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, \
+    MOE_ERR_HIP = range(6)
+MOE_F32, MOE_BF16, MOE_NVFP4 = 0, 1, 2
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4}
+
+EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_destroy",
+            "moe_status_string", "moe_profile_enable", "moe_profile_read", "moe_stage_name")
+MOE_NUM_STAGES = 10
+
+
+class MoEConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "d", "latent", "n_experts", "top_k", "ffn", "n_shared", "shared_ffn", "max_tokens",
+        "has_latent_proj", "act_dtype", "expert_dtype")]
+
+
+class MoEWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_down", "w_router", "b_router", "w1", "w2", "w1_scale", "w2_scale", "w1_gscale",
+        "w2_gscale", "w_up", "ws1", "ws2")]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+_LIB = None
+
+
+def lib(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises FileNotFoundError if it was not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise FileNotFoundError("libmoe.so not built at %s (run python -m sparse_moe_layer_fwd_amd.build)"
+                                % path)
+    L = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.moe_init.argtypes = [ctypes.POINTER(MoEConfig), ctypes.POINTER(MoEWeights), ctypes.POINTER(vp)]
+    L.moe_init.restype = ctypes.c_int
+    L.moe_workspace_size.argtypes = [vp, i32, ctypes.POINTER(sz)]
+    L.moe_workspace_size.restype = ctypes.c_int
+    L.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward.restype = ctypes.c_int
+    L.moe_destroy.argtypes = [vp]
+    L.moe_destroy.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_profile_enable.argtypes = [ctypes.c_int]
+    L.moe_profile_enable.restype = ctypes.c_int
+    L.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+    L.moe_profile_read.restype = ctypes.c_int
+    L.moe_stage_name.argtypes = [ctypes.c_int]
+    L.moe_stage_name.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def status_string(st: int) -> str:
+    return lib().moe_status_string(int(st)).decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != MOE_OK:
+        raise MoEError(st, where)
+
+
+def moe_init(cfg: MoEConfig, w: MoEWeights, check: bool = True):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = lib().moe_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    if check:
+        _check(st, "moe_init")
+    return st, h
+
+
+def moe_workspace_size(h, T: int, check: bool = True):
+    n = ctypes.c_size_t()
+    st = lib().moe_workspace_size(h, int(T), ctypes.byref(n))
+    if check:
+        _check(st, "moe_workspace_size")
+    return st, n.value
+
+
+def moe_route(h, x, T, idx, gate, counts, ws, ws_bytes, stream, check: bool = True) -> int:
+    st = lib().moe_route(h, x, int(T), idx, gate, counts, ws, int(ws_bytes), stream)
+    if check:
+        _check(st, "moe_route")
+    return st
+
+
+def moe_forward(h, x, T, y, idx, gate, counts, ws, ws_bytes, stream, check: bool = True) -> int:
+    st = lib().moe_forward(h, x, int(T), y, idx, gate, counts, ws, int(ws_bytes), stream)
+    if check:
+        _check(st, "moe_forward")
+    return st
+
+
+def moe_destroy(h) -> int:
+    return lib().moe_destroy(h)
+
+
+def moe_profile_enable(enable: bool) -> int:
+    st = lib().moe_profile_enable(1 if enable else 0)
+    _check(st, "moe_profile_enable")
+    return st
+
+
+def moe_profile_read():
+    """-> {stage name: (launches, total ms)}; clears the record."""
+    n = (ctypes.c_int32 * MOE_NUM_STAGES)()
+    ms = (ctypes.c_double * MOE_NUM_STAGES)()
+    _check(lib().moe_profile_read(n, ms), "moe_profile_read")
+    return {lib().moe_stage_name(i).decode(): (int(n[i]), float(ms[i])) for i in range(MOE_NUM_STAGES)}

@@ -1,0 +1,96 @@
+// Internal declarations shared by the HIP sources of libmoe.so (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// ------------------------------------------------------------------ conversions
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// two fp32 -> packed bf16x2 (lo in low half)
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// NVFP4 element: E2M1 code (4 bits) -> fp32, from the format's fields.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t mag = c & 7u;
+  uint32_t bits;
+  if (mag < 2u) bits = mag ? 0x3F000000u : 0u;            // 0, 0.5 (subnormal)
+  else bits = (((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+// NVFP4 block scale: E4M3 byte -> fp32 (bias 7; exponent field 0 is subnormal).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
+  return (b & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ kernel params
+enum Epi : int {
+  EPI_BF16 = 0,        // C(bf16) = acc
+  EPI_Z = 1,           // C(f32) = acc and C2(bf16) = acc             (latent z32 / z16)
+  EPI_SQRELU_BF16 = 2, // C(bf16) = max(g*acc,0)^2                    (expert up)
+  EPI_GATE_BF16 = 3,   // C(bf16) = row_scale[r]*g*acc                (expert down)
+  EPI_F32 = 4,         // C(f32) = acc (+ bias[col])                  (router, shared down)
+  EPI_BF16_ADD = 5,    // C(bf16) = acc + add[r][c] (fp32)            (up-proj + shared)
+  EPI_SQRELU_F32 = 6,  // C(f32) = max(acc,0)^2
+  EPI_GATE_F32 = 7,    // C(f32) = row_scale[r]*acc
+  EPI_F32_ADD = 8      // C(f32) = acc + add[r][c]
+};
+
+// A tile row source.  Logical row r of the GEMM reads physical row
+// a_rows ? a_rows[r] : r of A.
+struct GemmArgs {
+  const void* A; int64_t lda; const int* a_rows;
+  const void* B; int64_t ldb; int64_t b_gstride;     // element units (bf16/f32) or bytes (fp4 codes)
+  int32_t kseg; int64_t b_segstride;                  // k split into segments of kseg (shared W2)
+  const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;  // NVFP4 scales
+  const float* b_gscale;                              // NVFP4 per-group global scale
+  int32_t M, N, K;
+  const int4* tiles; const int* n_tiles;              // grouped: (group, row0, row1, -)
+  void* C; int64_t ldc; void* C2; int64_t ldc2;
+  const float* row_scale;                             // per logical row (gates)
+  const float* bias;                                  // per column
+  const float* add; int64_t ld_add;                   // fp32 addend
+};
+
+struct SkinnyArgs {
+  const uint16_t* A; int64_t lda; const int* a_rows;
+  const void* B; int64_t ldb; int64_t b_gstride;
+  const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;
+  const float* b_gscale;
+  int32_t N, K;
+  const int* counts; const int* offs;
+  uint16_t* C; int64_t ldc;
+  const float* row_scale;
+};
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int max_row_tiles,
+                            int grid_cap, hipStream_t s);
+hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
+                       int* chunk_counts, hipStream_t s);
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int* chunk_base,
+                       int* counts, int* offs, int4* tiles, int* n_tiles, hipStream_t s);
+hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
+                          const int* chunk_base, const int* offs, int* slot_token,
+                          float* slot_gate, int* tk_slot, hipStream_t s);
+hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot, int T, int K,
+                          int W, const float* add, void* out, bool out_f32, hipStream_t s);
+
+}  // namespace moe

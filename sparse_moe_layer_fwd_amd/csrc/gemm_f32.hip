@@ -1,0 +1,129 @@
+// fp32 GEMM on CDNA4 fp32 MFMA (v_mfma_f32_16x16x4_f32): the router GEMV
+// (logits = W_r z + b_r, kept in fp32 so that expert selection matches an exact
+// reference) and every GEMM of an all-fp32 layer.  Dense or grouped over a
+// device-side row-tile list, with an optional row gather on A.
+//
+// Tile 64x64x32, 256 threads = 4 wavefronts in a 2x2 grid, each 32x32 as 2x2
+// MFMA 16x16 blocks.  Operands are staged in LDS (padded rows).
+#include "common.h"
+
+namespace moe {
+
+template <bool ABF16, int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int BM = 64, BN = 64, BK = 32;
+  __shared__ float As[BM][BK + 1];
+  __shared__ float Bs[BN][BK + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = (p.N + BN - 1) / BN;
+  const int nrt = p.tiles ? *p.n_tiles : (p.M + BM - 1) / BM;
+  const int total = nrt * ntn;
+  const int lr = tid >> 2, kq = (tid & 3) * 8;
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int rt = item / ntn, nt = item - rt * ntn;
+    int g = 0, r0, r1;
+    if (p.tiles) {
+      const int4 tl = p.tiles[rt];
+      g = tl.x; r0 = tl.y; r1 = tl.z;
+    } else {
+      r0 = rt * BM; r1 = min(p.M, r0 + BM);
+    }
+    const int n0 = nt * BN;
+    int ar = min(r0 + lr, r1 - 1);
+    const int64_t arow = p.a_rows ? (int64_t)p.a_rows[ar] : (int64_t)ar;
+    const int bn = min(n0 + lr, p.N - 1);
+    const float* Bg = (const float*)p.B + (int64_t)g * p.b_gstride + (int64_t)bn * p.ldb;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < p.K; k0 += BK) {
+      float av[8], bv[8];
+      if (ABF16) {
+        const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)p.A + arow * p.lda + k0 + kq);
+        av[0] = bf2f(v.x & 0xFFFFu); av[1] = bf2f(v.x >> 16);
+        av[2] = bf2f(v.y & 0xFFFFu); av[3] = bf2f(v.y >> 16);
+        av[4] = bf2f(v.z & 0xFFFFu); av[5] = bf2f(v.z >> 16);
+        av[6] = bf2f(v.w & 0xFFFFu); av[7] = bf2f(v.w >> 16);
+      } else {
+        const float4* q = reinterpret_cast<const float4*>((const float*)p.A + arow * p.lda + k0 + kq);
+        const float4 x0 = q[0], x1 = q[1];
+        av[0] = x0.x; av[1] = x0.y; av[2] = x0.z; av[3] = x0.w;
+        av[4] = x1.x; av[5] = x1.y; av[6] = x1.z; av[7] = x1.w;
+      }
+      {
+        const int seg = k0 / p.kseg, kin = k0 - seg * p.kseg;
+        const float4* q = reinterpret_cast<const float4*>(Bg + (int64_t)seg * p.b_segstride + kin + kq);
+        const float4 x0 = q[0], x1 = q[1];
+        bv[0] = x0.x; bv[1] = x0.y; bv[2] = x0.z; bv[3] = x0.w;
+        bv[4] = x1.x; bv[5] = x1.y; bv[6] = x1.z; bv[7] = x1.w;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { As[lr][kq + i] = av[i]; Bs[lr][kq + i] = bv[i]; }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 4) {
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = As[wm * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = Bs[wn * 32 + j * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    // epilogue: D[i = 4*(lane/16) + r][j = lane%16] of each 16x16 block
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+          const int col = n0 + wn * 32 + j * 16 + (lane & 15);
+          if (row >= r1 || col >= p.N) continue;
+          float v = acc[i][j][r];
+          float* C = (float*)p.C + (int64_t)row * p.ldc + col;
+          if (EPI == EPI_F32) {
+            if (p.bias) v += p.bias[col];
+            *C = v;
+          } else if (EPI == EPI_SQRELU_F32) {
+            v = fmaxf(v, 0.0f);
+            *C = v * v;
+          } else if (EPI == EPI_GATE_F32) {
+            *C = p.row_scale[row] * v;
+          } else if (EPI == EPI_F32_ADD) {
+            *C = v + p.add[(int64_t)row * p.ld_add + col];
+          }
+        }
+  }
+}
+
+hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s) {
+  const int ntn = (a.N + 63) / 64;
+  const int nrt_max = a.tiles ? a.M : (a.M + 63) / 64;   // grouped: M carries the tile bound
+  int64_t total = (int64_t)nrt_max * ntn;
+  int grid = (int)(total < grid_cap ? total : grid_cap);
+  if (grid < 1) grid = 1;
+  dim3 g(grid), b(256);
+#define MOE_F32_CASE(AB, E) \
+  hipLaunchKernelGGL((gemm_f32_kernel<AB, E>), g, b, 0, s, a)
+  switch (epi) {
+    case EPI_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_F32); else MOE_F32_CASE(false, EPI_F32); break;
+    case EPI_SQRELU_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_SQRELU_F32); else MOE_F32_CASE(false, EPI_SQRELU_F32); break;
+    case EPI_GATE_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_GATE_F32); else MOE_F32_CASE(false, EPI_GATE_F32); break;
+    case EPI_F32_ADD: if (a_is_bf16) MOE_F32_CASE(true, EPI_F32_ADD); else MOE_F32_CASE(false, EPI_F32_ADD); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_F32_CASE
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,168 @@
+// Skinny grouped expert GEMM for small batches (decode: every expert sees at
+// most T <= 64 rows).  In this regime the layer is bound by streaming expert
+// weights from HBM (the pages: latency-bound serving of tens to hundreds of
+// tokens is dominated by expert weight traffic; Korean Nemotron 3 summary,
+// section 2.2 LatentMoE), so the kernel is built to keep many bytes of each
+// expert's weights in flight and touches every weight byte exactly once.
+//
+// Grid: (column tiles of 64, experts).  A block owns 64 output columns of one
+// expert; its 4 wavefronts split the reduction dimension in four and reduce
+// through LDS at the end.  Per step a lane loads 32 contiguous bytes of one
+// weight row (16 bf16, or 16 NVFP4 codes + their block scale) and the matching
+// 16 activations of each row block, and issues two v_mfma_f32_16x16x32_bf16 per
+// (row block, column block).  Both operands use the same permutation of the
+// reduction index inside a step, which leaves the dot products unchanged.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+__device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
+  const float lo = e2m1_to_f32(byte & 15u) * s;
+  const float hi = e2m1_to_f32((byte >> 4) & 15u) * s;
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+}  // namespace
+
+template <bool FP4, int EPI>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
+  constexpr int MAXRB = 4;                               // up to 64 rows per expert
+  __shared__ float red[3][MAXRB * 4][4][64];             // partial sums of waves 1..3
+  const int e = blockIdx.y;
+  const int cnt = p.counts[e];
+  if (cnt == 0) return;
+  const int row0 = p.offs[e];
+  const int nrb = (cnt + 15) >> 4;
+  const int n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kq = p.K >> 2;
+  const int kw0 = wave * kq;
+  const int grp = lane >> 4;                             // which 16-wide k slice of a 64-step
+
+  const uint16_t* arow[MAXRB];
+#pragma unroll
+  for (int rb = 0; rb < MAXRB; ++rb) {
+    const int r = rb * 16 + (lane & 15);
+    if (r < cnt) {
+      const int lr = row0 + r;
+      const int64_t pr = p.a_rows ? (int64_t)p.a_rows[lr] : (int64_t)lr;
+      arow[rb] = p.A + pr * p.lda;
+    } else {
+      arow[rb] = nullptr;
+    }
+  }
+  const uint8_t* brow[4];
+  const uint8_t* srow[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int n = min(n0 + cb * 16 + (lane & 15), p.N - 1);
+    if (FP4) {
+      brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb;
+      srow[cb] = p.b_scale + (int64_t)e * p.s_gstride + (int64_t)n * p.lds_scale;
+    } else {
+      brow[cb] = (const uint8_t*)((const uint16_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb);
+      srow[cb] = nullptr;
+    }
+  }
+
+  f32x4 acc[MAXRB][4];
+#pragma unroll
+  for (int rb = 0; rb < MAXRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 2
+  for (int kb = kw0; kb < kw0 + kq; kb += 64) {
+    const int k = kb + grp * 16;
+    uint4 b[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      if (FP4) {
+        const uint2 c = *reinterpret_cast<const uint2*>(brow[cb] + k / 2);
+        const float s = e4m3_to_f32(srow[cb][k / 16]);
+        b[cb][0] = make_uint4(fp4x2_bf(c.x & 0xFFu, s), fp4x2_bf((c.x >> 8) & 0xFFu, s),
+                              fp4x2_bf((c.x >> 16) & 0xFFu, s), fp4x2_bf(c.x >> 24, s));
+        b[cb][1] = make_uint4(fp4x2_bf(c.y & 0xFFu, s), fp4x2_bf((c.y >> 8) & 0xFFu, s),
+                              fp4x2_bf((c.y >> 16) & 0xFFu, s), fp4x2_bf(c.y >> 24, s));
+      } else {
+        const uint4* q = reinterpret_cast<const uint4*>((const uint16_t*)brow[cb] + k);
+        b[cb][0] = q[0];
+        b[cb][1] = q[1];
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < MAXRB; ++rb) {
+      if (rb < nrb) {
+        uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
+        if (arow[rb]) {
+          const uint4* q = reinterpret_cast<const uint4*>(arow[rb] + k);
+          a0 = q[0];
+          a1 = q[1];
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b[cb][0]), acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[cb][1]), acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int rb = 0; rb < MAXRB; ++rb)
+      if (rb < nrb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave - 1][rb * 4 + cb][i][lane] = acc[rb][cb][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const float gs = (FP4 && p.b_gscale) ? p.b_gscale[e] : 1.0f;
+#pragma unroll
+  for (int rb = 0; rb < MAXRB; ++rb) {
+    if (rb >= nrb) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + (lane >> 4) * 4 + i;     // D[i = 4*(lane/16) + r][j = lane%16]
+      if (r >= cnt) continue;
+      const int64_t orow = row0 + r;
+      float rsc = 1.0f;
+      if (EPI == EPI_GATE_BF16) rsc = p.row_scale[orow];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int col = n0 + cb * 16 + (lane & 15);
+        if (col >= p.N) continue;
+        float v = acc[rb][cb][i] + red[0][rb * 4 + cb][i][lane] + red[1][rb * 4 + cb][i][lane] +
+                  red[2][rb * 4 + cb][i][lane];
+        v *= gs;
+        uint16_t* C = p.C + orow * p.ldc + col;
+        if (EPI == EPI_SQRELU_BF16) {
+          const float h = fmaxf(v, 0.0f);
+          *C = (uint16_t)f2bf(h * h);
+        } else {
+          *C = (uint16_t)f2bf(rsc * v);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s) {
+  dim3 g((a.N + 63) / 64, n_experts), b(256);
+  if (b_nvfp4) {
+    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_SQRELU_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_GATE_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_GATE_BF16>), g, b, 0, s, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_SQRELU_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_GATE_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_GATE_BF16>), g, b, 0, s, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

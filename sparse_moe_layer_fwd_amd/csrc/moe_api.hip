@@ -1,0 +1,474 @@
+// Host side of libmoe.so: argument validation, the workspace layout, and the
+// launch sequence of the LatentMoE layer forward on the caller's stream.
+//
+// Dataflow (Korean Nemotron 3 summary, section 2.2 LatentMoE; notes.yuuk.io
+// Nemotron 3 note, method 2): x --(W_d, d->l)--> z --router--> top-K, gates
+// --> expert FFNs in l (grouped GEMMs over expert-sorted rows) --> gate-weighted
+// combine --(W_u, l->d)--> y.  A standard MoE (l = d) skips both projections;
+// shared experts run on x at d and are added to y (Nemotron 3 Nano blog,
+// granular MoE section).  No call synchronises the host; data-dependent
+// per-expert sizes stay on the device (tile list, counts, offsets).
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+using namespace moe;
+
+struct moe_handle {
+  moe_config_t c;
+  moe_weights_t w;
+  int device;
+  int num_cu;
+};
+
+namespace {
+
+constexpr int kTokensPerChunk = 64;   // routing chunk (histogram / scatter unit)
+constexpr int kPrefillBM = 128;       // grouped bf16 GEMM row-tile height
+constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
+constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- optional stage timing: a HIP event pair around each stage ----
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int stage; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[MOE_NUM_STAGES] = {};
+  double ms[MOE_NUM_STAGES] = {};
+};
+Prof& prof() {
+  static Prof* p = new Prof;   // never destroyed: safe at process exit
+  return *p;
+}
+hipEvent_t prof_event() {
+  Prof& P = prof();
+  if (!P.pool.empty()) {
+    hipEvent_t e = P.pool.back();
+    P.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+// Records the start of a stage; returns the index of its record or -1.
+int prof_begin(int stage, hipStream_t s) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  if (!P.on) return -1;
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return -1;
+  hipEventRecord(a, s);
+  P.pending.push_back({stage, a, b});
+  return (int)P.pending.size() - 1;
+}
+void prof_end(int rec, hipStream_t s) {
+  if (rec < 0) return;
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  if (rec < (int)P.pending.size()) hipEventRecord(P.pending[rec].b, s);
+}
+struct StageScope {
+  int rec;
+  hipStream_t s;
+  StageScope(int stage, hipStream_t st) : rec(prof_begin(stage, st)), s(st) {}
+  ~StageScope() { prof_end(rec, s); }
+};
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Plan {
+  size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, ntiles;
+  size_t slot_token, slot_gate, tk_slot, H, O, u, Hs, ys, total;
+  int nchunks, bm, max_row_tiles;
+  bool f32, skinny;
+};
+
+bool use_f32(const moe_config_t& c) { return c.act_dtype == MOE_F32; }
+
+bool use_skinny(const moe_config_t& c, int T) {
+  return !use_f32(c) && T <= kSkinnyMaxT && c.latent % 256 == 0 && c.ffn % 256 == 0;
+}
+
+Plan make_plan(const moe_config_t& c, int T) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  const size_t Tz = (size_t)T, N = (size_t)c.n_experts, K = (size_t)c.top_k;
+  const size_t L = (size_t)c.latent, M = (size_t)c.ffn, D = (size_t)c.d;
+  p.f32 = use_f32(c);
+  p.skinny = use_skinny(c, T);
+  const size_t es = p.f32 ? 4 : 2;
+  p.nchunks = (T + kTokensPerChunk - 1) / kTokensPerChunk;
+  p.bm = p.f32 ? kF32BM : kPrefillBM;
+  p.max_row_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
+  p.z32 = take(c.has_latent_proj ? Tz * L * 4 : 0);
+  p.z16 = take(c.has_latent_proj && !p.f32 ? Tz * L * 2 : 0);
+  p.logits = take(Tz * N * 4);
+  p.idx = take(Tz * K * 4);
+  p.gate = take(Tz * K * 4);
+  p.ccount = take((size_t)p.nchunks * N * 4);
+  p.cbase = take((size_t)p.nchunks * N * 4);
+  p.counts = take(N * 4);
+  p.offs = take((N + 1) * 4);
+  p.tiles = take((size_t)p.max_row_tiles * 16);
+  p.ntiles = take(4);
+  p.slot_token = take(Tz * K * 4);
+  p.slot_gate = take(Tz * K * 4);
+  p.tk_slot = take(Tz * K * 4);
+  p.H = take(Tz * K * M * es);
+  p.O = take(Tz * K * L * es);
+  p.u = take(c.has_latent_proj ? Tz * L * es : 0);
+  p.Hs = take(c.n_shared ? Tz * (size_t)c.n_shared * c.shared_ffn * es : 0);
+  p.ys = take(c.n_shared ? Tz * D * 4 : 0);
+  p.total = o;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>((char*)ws + off); }
+
+GemmArgs gemm_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kseg = 1 << 30;
+  return a;
+}
+
+int check_call(moe_handle_t h, const void* x, int32_t T, void* ws, size_t ws_bytes) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(h->c, T);
+  if (!ws || ws_bytes < p.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// Down-projection + router + top-K + bookkeeping.  Shared by route and forward.
+int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& p, hipStream_t s) {
+  const moe_config_t& c = h->c;
+  const moe_weights_t& w = h->w;
+  const int cap = h->num_cu * 2;
+  if (c.has_latent_proj) {
+    StageScope sc(MOE_STAGE_DOWN_PROJ, s);
+    GemmArgs a = gemm_args();
+    a.A = x; a.lda = c.d;
+    a.B = w.w_down; a.ldb = c.d;
+    a.M = T; a.N = c.latent; a.K = c.d;
+    a.C = at<void>(ws, p.z32); a.ldc = c.latent;
+    if (p.f32) {
+      MOE_TRY(launch_gemm_f32(a, false, EPI_F32, cap, s));
+    } else {
+      a.C2 = at<void>(ws, p.z16); a.ldc2 = c.latent;
+      MOE_TRY(launch_gemm_bf16(a, false, EPI_Z, kPrefillBM, 0, cap, s));
+    }
+  }
+  {
+    StageScope sc(MOE_STAGE_ROUTER, s);
+    GemmArgs a = gemm_args();
+    a.A = c.has_latent_proj ? (const void*)at<float>(ws, p.z32) : x;
+    a.lda = c.latent;
+    a.B = w.w_router; a.ldb = c.latent;
+    a.M = T; a.N = c.n_experts; a.K = c.latent;
+    a.C = at<float>(ws, p.logits); a.ldc = c.n_experts;
+    a.bias = w.b_router;
+    const bool a_bf16 = !c.has_latent_proj && c.act_dtype == MOE_BF16;
+    MOE_TRY(launch_gemm_f32(a, a_bf16, EPI_F32, cap, s));
+  }
+  {
+    StageScope sc(MOE_STAGE_TOPK, s);
+    MOE_TRY(launch_topk(at<float>(ws, p.logits), T, c.n_experts, c.top_k, kTokensPerChunk,
+                        at<int>(ws, p.idx), at<float>(ws, p.gate), at<int>(ws, p.ccount), s));
+  }
+  StageScope sc(MOE_STAGE_SCAN, s);
+  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, at<int>(ws, p.cbase),
+                      at<int>(ws, p.counts), at<int>(ws, p.offs), at<int4>(ws, p.tiles),
+                      at<int>(ws, p.ntiles), s));
+  return MOE_OK;
+}
+
+int copy_out(moe_handle_t h, int T, const void* ws, const Plan& p, int32_t* idx, float* gate,
+             int32_t* counts, hipStream_t s) {
+  const size_t tk = (size_t)T * h->c.top_k;
+  if (idx) MOE_TRY(hipMemcpyAsync(idx, (const char*)ws + p.idx, tk * 4, hipMemcpyDeviceToDevice, s));
+  if (gate) MOE_TRY(hipMemcpyAsync(gate, (const char*)ws + p.gate, tk * 4, hipMemcpyDeviceToDevice, s));
+  if (counts)
+    MOE_TRY(hipMemcpyAsync(counts, (const char*)ws + p.counts, (size_t)h->c.n_experts * 4,
+                           hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+// One grouped expert GEMM (up: sqrelu epilogue; down: gate epilogue).
+int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const void* A,
+                        const int* a_rows, void* C, hipStream_t s) {
+  const moe_config_t& c = h->c;
+  const moe_weights_t& w = h->w;
+  const int64_t rows = up ? c.ffn : c.latent;     // output columns
+  const int64_t kdim = up ? c.latent : c.ffn;     // reduction
+  const bool fp4 = c.expert_dtype == MOE_NVFP4;
+  const void* B = up ? w.w1 : w.w2;
+  const uint8_t* S = up ? w.w1_scale : w.w2_scale;
+  const float* G = up ? w.w1_gscale : w.w2_gscale;
+  const int cap = h->num_cu * 2;
+  StageScope sc(up ? MOE_STAGE_EXPERT_UP : MOE_STAGE_EXPERT_DOWN, s);
+  if (p.skinny) {
+    SkinnyArgs a;
+    memset(&a, 0, sizeof(a));
+    a.A = (const uint16_t*)A; a.lda = kdim; a.a_rows = a_rows;
+    a.B = B;
+    a.ldb = fp4 ? kdim / 2 : kdim;
+    a.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
+    a.b_scale = S; a.lds_scale = kdim / 16; a.s_gstride = rows * kdim / 16;
+    a.b_gscale = G;
+    a.N = (int)rows; a.K = (int)kdim;
+    a.counts = at<int>(ws, p.counts); a.offs = at<int>(ws, p.offs);
+    a.C = (uint16_t*)C; a.ldc = rows;
+    a.row_scale = at<float>(ws, p.slot_gate);
+    MOE_TRY(launch_skinny(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, c.n_experts, s));
+    return MOE_OK;
+  }
+  GemmArgs a = gemm_args();
+  a.A = A; a.lda = kdim; a.a_rows = a_rows;
+  a.B = B;
+  a.ldb = fp4 ? kdim / 2 : kdim;
+  a.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
+  a.b_scale = S; a.lds_scale = kdim / 16; a.s_gstride = rows * kdim / 16;
+  a.b_gscale = G;
+  a.N = (int)rows; a.K = (int)kdim;
+  a.tiles = at<int4>(ws, p.tiles); a.n_tiles = at<int>(ws, p.ntiles);
+  a.C = C; a.ldc = rows;
+  a.row_scale = at<float>(ws, p.slot_gate);
+  if (p.f32) {
+    a.M = p.max_row_tiles;   // grouped: upper bound on row tiles (grid sizing)
+    MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_GATE_F32, cap, s));
+  } else {
+    MOE_TRY(launch_gemm_bf16(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, kPrefillBM,
+                             p.max_row_tiles, cap, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported shape or dtype combination";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_NO_DEVICE: return "MOE_ERR_NO_DEVICE: no HIP device visible";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime call or kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out) {
+  if (!cfg || !w || !out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const moe_config_t& c = *cfg;
+  if (c.d <= 0 || c.latent <= 0 || c.ffn <= 0 || c.max_tokens <= 0) return MOE_ERR_INVALID_ARG;
+  if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts) return MOE_ERR_INVALID_ARG;
+  if (c.n_shared < 0 || (c.n_shared > 0 && c.shared_ffn <= 0)) return MOE_ERR_INVALID_ARG;
+  if (c.has_latent_proj != 0 && c.has_latent_proj != 1) return MOE_ERR_INVALID_ARG;
+  if (!c.has_latent_proj && c.latent != c.d) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)c.max_tokens * c.top_k > (1 << 30)) return MOE_ERR_INVALID_ARG;
+  if (c.act_dtype != MOE_F32 && c.act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c.expert_dtype != MOE_F32 && c.expert_dtype != MOE_BF16 && c.expert_dtype != MOE_NVFP4)
+    return MOE_ERR_INVALID_ARG;
+  if (c.n_experts > 1024 || c.top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (c.d % 64 || c.latent % 64 || c.ffn % 64 || (c.n_shared && c.shared_ffn % 64))
+    return MOE_ERR_UNSUPPORTED;
+  if ((c.act_dtype == MOE_F32) != (c.expert_dtype == MOE_F32)) return MOE_ERR_UNSUPPORTED;
+  // weights
+  if (!w->w_router || !aligned16(w->w_router) || !w->w1 || !aligned16(w->w1) || !w->w2 ||
+      !aligned16(w->w2))
+    return MOE_ERR_INVALID_ARG;
+  if (w->b_router && !aligned16(w->b_router)) return MOE_ERR_INVALID_ARG;
+  if (c.has_latent_proj) {
+    if (!w->w_down || !aligned16(w->w_down) || !w->w_up || !aligned16(w->w_up))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (c.expert_dtype == MOE_NVFP4) {
+    if (!w->w1_scale || !w->w2_scale || !w->w1_gscale || !w->w2_gscale ||
+        !aligned16(w->w1_scale) || !aligned16(w->w2_scale))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (c.n_shared) {
+    if (!w->ws1 || !aligned16(w->ws1) || !w->ws2 || !aligned16(w->ws2)) return MOE_ERR_INVALID_ARG;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return MOE_ERR_NO_DEVICE;
+  }
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  moe_handle* h = new (std::nothrow) moe_handle;
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->c = c;
+  h->w = *w;
+  h->device = dev;
+  h->num_cu = ncu > 0 ? ncu : 256;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_workspace_size(moe_handle_t h, int32_t T, size_t* bytes) {
+  if (!h || !bytes || T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
+  *bytes = T == 0 ? 0 : make_plan(h->c, T).total;
+  return MOE_OK;
+}
+
+int moe_profile_enable(int enable) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = enable != 0;
+  return MOE_OK;
+}
+
+int moe_profile_read(int32_t* launches, double* ms) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  int st = MOE_OK;
+  for (auto& r : P.pending) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      st = MOE_ERR_HIP;
+    } else {
+      P.launches[r.stage] += 1;
+      P.ms[r.stage] += t;
+    }
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.pending.clear();
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    if (launches) launches[i] = (int32_t)P.launches[i];
+    if (ms) ms[i] = P.ms[i];
+    P.launches[i] = 0;
+    P.ms[i] = 0.0;
+  }
+  return st;
+}
+
+const char* moe_stage_name(int stage) {
+  static const char* names[MOE_NUM_STAGES] = {"down_proj", "router", "topk", "scan", "scatter",
+                                              "expert_up", "expert_down", "shared", "combine",
+                                              "up_proj"};
+  return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "unknown";
+}
+
+int moe_destroy(moe_handle_t h) {
+  delete h;
+  return MOE_OK;
+}
+
+int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gate,
+              int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_call(h, x, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!idx || !gate || !counts || !aligned16(idx) || !aligned16(gate) || !aligned16(counts))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const Plan p = make_plan(h->c, T);
+  st = enqueue_routing(h, x, T, ws, p, s);
+  if (st != MOE_OK) return st;
+  return copy_out(h, T, ws, p, idx, gate, counts, s);
+}
+
+int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
+                int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_call(h, x, T, ws, ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if ((idx && !aligned16(idx)) || (gate && !aligned16(gate)) || (counts && !aligned16(counts)))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const moe_config_t& c = h->c;
+  const moe_weights_t& w = h->w;
+  const Plan p = make_plan(c, T);
+  const int cap = h->num_cu * 2;
+  st = enqueue_routing(h, x, T, ws, p, s);
+  if (st != MOE_OK) return st;
+  {
+    StageScope sc(MOE_STAGE_SCATTER, s);
+    MOE_TRY(launch_scatter(at<int>(ws, p.idx), at<float>(ws, p.gate), T, c.top_k, c.n_experts,
+                           kTokensPerChunk, at<int>(ws, p.cbase), at<int>(ws, p.offs),
+                           at<int>(ws, p.slot_token), at<float>(ws, p.slot_gate),
+                           at<int>(ws, p.tk_slot), s));
+  }
+  // expert FFNs over expert-sorted rows
+  const void* zsrc = c.has_latent_proj ? (p.f32 ? (const void*)at<float>(ws, p.z32)
+                                                : (const void*)at<uint16_t>(ws, p.z16))
+                                       : x;
+  st = enqueue_expert_gemm(h, p, ws, true, zsrc, at<int>(ws, p.slot_token), at<void>(ws, p.H), s);
+  if (st != MOE_OK) return st;
+  st = enqueue_expert_gemm(h, p, ws, false, at<void>(ws, p.H), nullptr, at<void>(ws, p.O), s);
+  if (st != MOE_OK) return st;
+  // shared experts at d: Hs = sqrelu(x Ws1^T), ys = Hs Ws2^T (fp32)
+  const float* ys = nullptr;
+  if (c.n_shared) {
+    StageScope sc(MOE_STAGE_SHARED, s);
+    const int sm = c.n_shared * c.shared_ffn;
+    GemmArgs a = gemm_args();
+    a.A = x; a.lda = c.d;
+    a.B = w.ws1; a.ldb = c.d;
+    a.M = T; a.N = sm; a.K = c.d;
+    a.C = at<void>(ws, p.Hs); a.ldc = sm;
+    if (p.f32) MOE_TRY(launch_gemm_f32(a, false, EPI_SQRELU_F32, cap, s));
+    else MOE_TRY(launch_gemm_bf16(a, false, EPI_SQRELU_BF16, kPrefillBM, 0, cap, s));
+    GemmArgs b = gemm_args();
+    b.A = at<void>(ws, p.Hs); b.lda = sm;
+    b.B = w.ws2; b.ldb = c.shared_ffn;
+    b.kseg = c.shared_ffn; b.b_segstride = (int64_t)c.d * c.shared_ffn;
+    b.M = T; b.N = c.d; b.K = sm;
+    b.C = at<float>(ws, p.ys); b.ldc = c.d;
+    if (p.f32) MOE_TRY(launch_gemm_f32(b, false, EPI_F32, cap, s));
+    else MOE_TRY(launch_gemm_bf16(b, false, EPI_F32, kPrefillBM, 0, cap, s));
+    ys = at<float>(ws, p.ys);
+  }
+  if (c.has_latent_proj) {
+    {
+      StageScope sc(MOE_STAGE_COMBINE, s);
+      MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot), T,
+                             c.top_k, c.latent, nullptr, at<void>(ws, p.u), p.f32, s));
+    }
+    StageScope sc(MOE_STAGE_UP_PROJ, s);
+    GemmArgs a = gemm_args();
+    a.A = at<void>(ws, p.u); a.lda = c.latent;
+    a.B = w.w_up; a.ldb = c.latent;
+    a.M = T; a.N = c.d; a.K = c.latent;
+    a.C = y; a.ldc = c.d;
+    a.add = ys; a.ld_add = c.d;
+    if (p.f32) MOE_TRY(launch_gemm_f32(a, false, ys ? EPI_F32_ADD : EPI_F32, cap, s));
+    else MOE_TRY(launch_gemm_bf16(a, false, ys ? EPI_BF16_ADD : EPI_BF16, kPrefillBM, 0, cap, s));
+  } else {
+    StageScope sc(MOE_STAGE_COMBINE, s);
+    MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot), T, c.top_k,
+                           c.d, ys, y, p.f32, s));
+  }
+  return copy_out(h, T, ws, p, idx, gate, counts, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,267 @@
+// Routing kernels: wavefront top-K + softmax with per-chunk expert histograms,
+// the expert offset scan (+ grouped-GEMM tile list), the stable scatter into
+// expert-sorted slots, and the deterministic gather-reduce combine.
+//
+// Top-K selection and the softmax over the selected logits follow the routed
+// MoE of the pages (K of N experts per token: 6 of 128 in the Nemotron 3 Nano
+// blog's granular MoE section, 22 of 512 in the Ultra release news); the gate
+// function, the tie rule and the dropless policy are readings (see moe.h).
+#include "common.h"
+
+namespace moe {
+
+// Orderable key: larger logit first, then lower expert id.  Invalid lanes are 0.
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t e) {
+  if (v == 0.0f) v = 0.0f;                                 // -0 ties with +0
+  uint32_t u = __float_as_uint(v);
+  u ^= (u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u ^= (u & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint32_t key_expert(uint64_t k) {
+  return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One block per chunk of `tc` tokens; one wavefront per token.  Each lane holds
+// the logits of experts lane, lane+64, ...; K rounds of a wave-wide max over
+// packed (value, id) keys give the K largest in descending order.
+template <int NJ>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int N,
+                                                   int K, int tc, int* __restrict__ idx,
+                                                   float* __restrict__ gate,
+                                                   int* __restrict__ chunk_counts) {
+  __shared__ int hist[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < N; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int c = blockIdx.x;
+  const int t_end = min(T, (c + 1) * tc);
+  for (int t = c * tc + wave; t < t_end; t += 4) {
+    uint64_t key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * 64 + lane;
+      key[j] = e < N ? make_key(logits[(int64_t)t * N + e], (uint32_t)e) : 0ull;
+    }
+    uint32_t taken = 0;
+    uint64_t mine = 0;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = 0;
+      int bj = -1;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (!((taken >> j) & 1u) && key[j] > best) { best = key[j]; bj = j; }
+      const uint64_t w = wave_max_u64(best);
+      if (bj >= 0 && best == w) taken |= 1u << bj;
+      if (lane == k) mine = w;
+    }
+    const float v = key_value(mine);
+    const float vmax = __shfl(v, 0, 64);
+    float ex = lane < K ? expf(v - vmax) : 0.0f;
+    float s = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane < K) {
+      const uint32_t e = key_expert(mine);
+      idx[(int64_t)t * K + lane] = (int)e;
+      gate[(int64_t)t * K + lane] = ex / s;
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += 256) chunk_counts[(int64_t)c * N + i] = hist[i];
+}
+
+hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
+                       int* chunk_counts, hipStream_t s) {
+  const int nchunks = (T + tc - 1) / tc;
+  dim3 g(nchunks), b(256);
+  if (N <= 64) hipLaunchKernelGGL(topk_kernel<1>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
+  else if (N <= 128) hipLaunchKernelGGL(topk_kernel<2>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
+  else if (N <= 256) hipLaunchKernelGGL(topk_kernel<4>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
+  else if (N <= 512) hipLaunchKernelGGL(topk_kernel<8>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
+  else hipLaunchKernelGGL(topk_kernel<16>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
+  return hipGetLastError();
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads).
+__device__ int block_excl_scan_1024(int v, int* total_out) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(x, off, 64);
+    if (lane >= off) x += o;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) base += wsum[w];
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total_out = tot;
+  return base + x - v;
+}
+
+// Single block: per-expert totals over chunks (chunk_base = exclusive prefix
+// over chunks), expert offsets, and the row-tile list of height bm.
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_counts,
+                                                    int nchunks, int N, int bm,
+                                                    int* __restrict__ chunk_base,
+                                                    int* __restrict__ counts,
+                                                    int* __restrict__ offs,
+                                                    int4* __restrict__ tiles,
+                                                    int* __restrict__ n_tiles) {
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < N) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_counts[(int64_t)c * N + e];
+      chunk_base[(int64_t)c * N + e] = total;
+      total += v;
+    }
+  }
+  int all = 0;
+  const int off = block_excl_scan_1024(total, &all);
+  const int nt = bm > 0 ? (total + bm - 1) / bm : 0;
+  int all_tiles = 0;
+  const int toff = block_excl_scan_1024(nt, &all_tiles);
+  if (e < N) {
+    counts[e] = total;
+    offs[e] = off;
+    if (e == N - 1) offs[N] = off + total;
+    for (int i = 0; i < nt; ++i)
+      tiles[toff + i] = make_int4(e, off + i * bm, min(off + total, off + (i + 1) * bm), 0);
+  }
+  if (e == 0) n_tiles[0] = all_tiles;
+}
+
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int* chunk_base,
+                       int* counts, int* offs, int4* tiles, int* n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm,
+                     chunk_base, counts, offs, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+// One wavefront per chunk; assignments (t, k) are visited in order, so within an
+// expert the slots follow (t, k) order: a stable, deterministic scatter.
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx,
+                                                     const float* __restrict__ gate, int T, int K,
+                                                     int N, int tc,
+                                                     const int* __restrict__ chunk_base,
+                                                     const int* __restrict__ offs,
+                                                     int* __restrict__ slot_token,
+                                                     float* __restrict__ slot_gate,
+                                                     int* __restrict__ tk_slot) {
+  __shared__ int cnt[1024];
+  const int c = blockIdx.x, lane = threadIdx.x;
+  for (int i = lane; i < N; i += 64) cnt[i] = offs[i] + chunk_base[(int64_t)c * N + i];
+  __syncthreads();
+  const int64_t a0 = (int64_t)c * tc * K;
+  const int64_t a1 = (int64_t)min(T, (c + 1) * tc) * K;
+  for (int64_t base = a0; base < a1; base += 64) {
+    const int64_t a = base + lane;
+    const bool valid = a < a1;
+    const int e = valid ? idx[a] : -1;
+    int rank = 0, tot = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __shfl(e, j, 64);
+      if (ej == e) { ++tot; if (j < lane) ++rank; }
+    }
+    const int slot = valid ? cnt[e] + rank : 0;
+    __syncthreads();
+    if (valid && rank == 0) cnt[e] += tot;
+    __syncthreads();
+    if (valid) {
+      slot_token[slot] = (int)(a / K);
+      slot_gate[slot] = gate[a];
+      tk_slot[a] = slot;
+    }
+  }
+}
+
+hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
+                          const int* chunk_base, const int* offs, int* slot_token,
+                          float* slot_gate, int* tk_slot, hipStream_t s) {
+  const int nchunks = (T + tc - 1) / tc;
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, idx, gate, T, K, N, tc,
+                     chunk_base, offs, slot_token, slot_gate, tk_slot);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ combine
+// out[t][c] = add[t][c] + sum_{k=0..K-1} O[tk_slot[t][k]][c], summed in fp32 in
+// that fixed order (no atomics), then stored once.  8 columns per thread.
+template <bool OF32, bool OUTF32>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O, int64_t ldo,
+                                                      const int* __restrict__ tk_slot, int K, int W,
+                                                      const float* __restrict__ add,
+                                                      void* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int c0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c0 >= W) return;
+  float acc[8];
+  if (add) {
+    const float4* p = reinterpret_cast<const float4*>(add + (int64_t)t * W + c0);
+    float4 a = p[0], b = p[1];
+    acc[0] = a.x; acc[1] = a.y; acc[2] = a.z; acc[3] = a.w;
+    acc[4] = b.x; acc[5] = b.y; acc[6] = b.z; acc[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  }
+  const int* sl = tk_slot + (int64_t)t * K;
+  for (int k = 0; k < K; ++k) {
+    const int64_t s = sl[k];
+    if (OF32) {
+      const float4* p = reinterpret_cast<const float4*>((const float*)O + s * ldo + c0);
+      float4 a = p[0], b = p[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)O + s * ldo + c0);
+      acc[0] += bf2f(v.x & 0xFFFFu); acc[1] += bf2f(v.x >> 16);
+      acc[2] += bf2f(v.y & 0xFFFFu); acc[3] += bf2f(v.y >> 16);
+      acc[4] += bf2f(v.z & 0xFFFFu); acc[5] += bf2f(v.z >> 16);
+      acc[6] += bf2f(v.w & 0xFFFFu); acc[7] += bf2f(v.w >> 16);
+    }
+  }
+  if (OUTF32) {
+    float4* p = reinterpret_cast<float4*>((float*)out + (int64_t)t * W + c0);
+    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+    uint4 v;
+    v.x = pack_bf2(acc[0], acc[1]); v.y = pack_bf2(acc[2], acc[3]);
+    v.z = pack_bf2(acc[4], acc[5]); v.w = pack_bf2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>((uint16_t*)out + (int64_t)t * W + c0) = v;
+  }
+}
+
+hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot, int T, int K,
+                          int W, const float* add, void* out, bool out_f32, hipStream_t s) {
+  dim3 g(T, (W + 2047) / 2048), b(256);
+  if (o_f32 && out_f32) hipLaunchKernelGGL((combine_kernel<true, true>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
+  else if (o_f32) hipLaunchKernelGGL((combine_kernel<true, false>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
+  else if (out_f32) hipLaunchKernelGGL((combine_kernel<false, true>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
+  else hipLaunchKernelGGL((combine_kernel<false, false>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -136,11 +136,16 @@ _TID = {"x": 1, "x_redraw": 2, "w_down": 3, "w_router": 4, "b_router": 5, "w1": 
         "w2": 7, "w_up": 8, "ws1": 9, "ws2": 10, "nvfp4_w1": 11, "nvfp4_w2": 12}
 
 # NVFP4 test weights are drawn directly as codes (no quantiser is needed: the
-# oracle and the kernels both consume the same packed bits).
-# Magnitude-code probabilities for E2M1 codes 0..7 (a bell-like shape).
-_E2M1_MAG_P = np.array([0.12, 0.20, 0.18, 0.15, 0.12, 0.12, 0.07, 0.04])
-# E4M3 scale bytes: exponent field 5..8, any mantissa (positive, finite).
-_E4M3_EXP_FIELDS = np.array([5, 6, 7, 8], dtype=np.uint8)
+# oracle and the kernels both consume the same packed bits).  One random byte
+# per element: its low 7 bits pick the E2M1 magnitude code 0..7 through a
+# 128-entry table (bell-like frequencies 15,26,23,19,16,15,9,5 out of 128), its
+# top bit is the sign.
+_E2M1_MAG_LUT = np.repeat(np.arange(8, dtype=np.uint8),
+                          np.array([15, 26, 23, 19, 16, 15, 9, 5]))
+assert _E2M1_MAG_LUT.size == 128
+# E4M3 block-scale bytes: exponent field 5..8 and any mantissa (positive, finite,
+# values 0.25 .. 3.75).  One random byte per block: bits 0-1 -> exponent field
+# - 5, bits 2-4 -> mantissa.
 # Global scale = _NVFP4_C / sqrt(fan_in) keeps the decoded weights near
 # N(0, 1/fan_in) in spread (element rms of code*scale is about 3.5).
 _NVFP4_C = 0.3
@@ -236,15 +241,13 @@ class Workload:
     # ------------------------------------------------------------ expert weights
     def _nvfp4(self, name: str, e: int, rows: int, cols: int):
         g = self._rng(name, e)
-        mag = g.choice(8, size=(rows, cols), p=_E2M1_MAG_P).astype(np.uint8)
-        sign = g.integers(0, 2, size=(rows, cols), dtype=np.uint8)
-        code = mag | (sign << 3)
+        r = g.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        code = _E2M1_MAG_LUT[r & 127] | ((r >> 7) << 3)
         packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
         nb = cols // 16
         srows = (rows + 15) // 16 if self.nvfp4_2d_blocks else rows
-        ef = g.choice(_E4M3_EXP_FIELDS, size=(srows, nb))
-        mf = g.integers(0, 8, size=(srows, nb), dtype=np.uint8)
-        scales = ((ef << 3) | mf).astype(np.uint8)
+        sb = g.integers(0, 256, size=(srows, nb), dtype=np.uint8)
+        scales = ((((sb & 3) + 5) << 3) | ((sb >> 2) & 7)).astype(np.uint8)
         if self.nvfp4_2d_blocks:        # one scale per 16x16 block
             scales = np.repeat(scales, 16, axis=0)[:rows]
         gscale = np.float32(_NVFP4_C / math.sqrt(cols))

@@ -71,34 +71,4 @@ def f64_layer(cfg: MoEConfig, rng: np.random.Generator, T=None):
     return c, ArrayLayer(c, x, wr, w1, w2, wd, wu, None, ws1, ws2)
 
 
-def margin_filter(wl, cfg, max_rounds=20):
-    """Redraw tokens whose fp64 top-K gap is below cfg.margin (the configs ask for
-    routing inputs without near-ties).  Uses the oracle's routing; returns the
-    number of rows redrawn.  The redraws come from the generator's per-(token,
-    attempt) streams, so the result is reproducible."""
-    import oracle
-    if cfg.top_k >= cfg.n_experts:
-        return 0
-    x = np.array(wl.x(), copy=True)
-    wd = wl.w_down()
-    wd64 = None if wd is None else oracle.decode_expert(wd, cfg.act)
-    wr, br = wl.w_router(), wl.b_router()
-    redrawn = 0
-    attempt = np.zeros(cfg.T, dtype=np.int64)
-    bad = np.arange(cfg.T)
-    for _ in range(max_rounds):
-        z = oracle.latent_down(oracle.decode_expert(x[bad], cfg.act), wd64)
-        lg = oracle.router_logits(z, wr, br)
-        srt = -np.sort(-lg, axis=1)
-        gap = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k]
-        bad = bad[gap < cfg.margin]
-        if bad.size == 0:
-            break
-        for t in bad:
-            attempt[t] += 1
-            x[t] = wl.x_redraw(int(t), int(attempt[t]))
-            redrawn += 1
-    else:
-        raise RuntimeError("margin filter did not converge")
-    wl.set_x(x)
-    return redrawn
+from oracle.margin import margin_filter  # noqa: E402,F401
