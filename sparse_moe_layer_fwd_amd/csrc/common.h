@@ -60,6 +60,7 @@ struct GemmArgs {
   const float* b_gscale;                              // NVFP4 per-group global scale
   int32_t M, N, K;
   const int4* tiles; const int* n_tiles;              // grouped: (group, row0, row1, -)
+  const int4* tiles2;                                 // grouped: second (remainder) list
   void* C; int64_t ldc; void* C2; int64_t ldc2;
   const float* row_scale;                             // per logical row (gates)
   const float* bias;                                  // per column
@@ -80,13 +81,14 @@ struct SkinnyArgs {
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s);
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int max_row_tiles,
-                            int grid_cap, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
+                            int64_t max_items, int grid_cap, hipStream_t s);
 hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int* chunk_base,
-                       int* counts, int* offs, int4* tiles, int* n_tiles, hipStream_t s);
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int* chunk_base,
+                       int* counts, int* offs, int4* tiles, int4* tiles2, int* n_tiles,
+                       hipStream_t s);
 hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
                           const int* chunk_base, const int* offs, int* slot_token,
                           float* slot_gate, int* tk_slot, hipStream_t s);

@@ -2,25 +2,61 @@
 // the latent projections d -> l and l -> d, the shared experts, and the grouped
 // expert GEMMs of the prefill path.
 //
-// Grouped mode walks a device-side list of row tiles (expert, row0, row1) made
-// by the routing scan, so no host round-trip is needed for the data-dependent
-// expert sizes.  The A tile can be gathered through a row map (the expert up
-// GEMM reads latent rows straight from z by token id).  B is bf16 or NVFP4:
-// NVFP4 codes (E2M1, 16-element E4M3 block scales, FP32 global scale: Korean
-// Nemotron 3 summary, section 2.4 NVFP4 Training) are decoded exactly to bf16
-// while staging into LDS (every e2m1*e4m3 product is a bf16 value); the global
-// scale multiplies the fp32 accumulator in the epilogue.
+// C[r][n] = epilogue( sum_k A[row(r)][k] * B_g[n][k] ).  Grouped mode walks a
+// device-side list of row tiles (expert g, row0, row1) made by the routing
+// scan, so the data-dependent expert sizes never need a host round-trip.  The A
+// rows can be gathered through a row map (the expert up GEMM reads latent rows
+// straight from z by token id).  B is bf16 or NVFP4: NVFP4 codes (E2M1 values,
+// 16-element E4M3 block scales, FP32 global scale; Korean Nemotron 3 summary,
+// section 2.4 NVFP4 Training) are decoded exactly to bf16 inside LDS once per
+// block and k-tile (every e2m1*e4m3 product is a bf16 value); the global scale
+// multiplies the fp32 accumulator in the epilogue.
 //
-// Tile BM x BN x 64, 256 threads = 4 wavefronts (2x2), each (BM/2) x (BN/2) in
-// 32x32 MFMA blocks.  LDS is double-buffered: global loads of tile k+1 are in
-// flight while tile k is multiplied.  Rows of 64 bf16 (8 chunks of 16 bytes)
-// are stored with chunk index XOR (row & 7) so that a wavefront's 16-byte
-// fragment reads spread over all banks.
+// Data movement: operands go global -> LDS with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
+// through a ring of NST stages, so NST-1 k-tiles are in flight while one is
+// multiplied and no VGPRs are spent on staging.  Each wavefront waits for its
+// own loads with an explicit vmcnt, then a bare s_barrier publishes the stage.
+// LDS rows hold BK bf16 as 16-byte chunks; chunk c of row r sits at c ^ f(r),
+// which spreads the fragment reads of 8 or 16 consecutive rows over distinct
+// bank groups.  The swizzle is applied on the global side (which chunk a lane
+// fetches) because the LDS side of a direct load is fixed by the lane id.
+//
+// Tile BM x BN, WGM x WGN wavefronts, each owning (BM/WGM) x (BN/WGN) in 32x32
+// MFMA blocks.  The MFMA computes C^T (weights as the A operand, activations as
+// the B operand) so each lane holds 4 consecutive output columns of one row:
+// 8- or 16-byte stores.
 #include "common.h"
 
 namespace moe {
 
 namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// barrier without the compiler's implied vmcnt(0): LDS-DMA completion is
+// tracked by the explicit vmcnt waits above
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+// barrier after this wavefront's own LDS writes
+__device__ __forceinline__ void bar_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// chunk swizzle for rows of CPR 16-byte chunks (conflict-free for 32 or 64 banks)
+template <int CPR>
+__device__ __forceinline__ int swz_chunk(int row, int c) {
+  if (CPR == 8) return c ^ ((row & 7) ^ ((row >> 3) & 1));
+  return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
+}
 
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t byte, float s) {
   const float lo = e2m1_to_f32(byte & 15u) * s;
@@ -41,214 +77,339 @@ __device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, float s, uin
   o1.w = fp4x2_to_bf16x2(w1 >> 24, s);
 }
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
-
 }  // namespace
 
-template <int BM, int BN, bool FP4, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int A_CH = BM * 8 / 256;              // 16-byte A chunks per thread
-  constexpr int B_CH = FP4 ? BN * 2 / 256 : BN * 8 / 256;
-  constexpr int TM = BM / 64, TN = BN / 64;       // 32x32 blocks per wavefront
-  __shared__ uint4 smem[2][(BM + BN) * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ntn = (p.N + BN - 1) / BN;
-  const int nrt = p.tiles ? *p.n_tiles : (p.M + BM - 1) / BM;
-  const int total = nrt * ntn;
-  const int nk = p.K / 64;
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+struct TileCfg {
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int CPR = BK / 8;                          // 16-byte chunks per bf16 row
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int BQ_BYTES = BN * BK / 2;                 // NVFP4 codes
+  static constexpr int BS_BYTES = BN * BK / 16;                // NVFP4 scales
+  static constexpr int B_BYTES = FP4 ? BQ_BYTES + BS_BYTES : BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int BDQ = FP4 ? BN * BK * 2 : 0;            // decoded B (double-buffered)
+  static constexpr int LDS = NST * STAGE + 2 * BDQ;
+  static constexpr int A_TOT = BM * CPR / 64;                  // 1 KB DMA blocks per k-tile
+  static constexpr int B_TOT = FP4 ? BQ_BYTES / 1024 : BN * CPR / 64;
+  static constexpr int S_TOT = FP4 ? BS_BYTES / 256 : 0;       // 4-byte-per-lane blocks
+  static constexpr int A_PW = (A_TOT + NW - 1) / NW;           // per wavefront
+  static constexpr int B_PW = (B_TOT + NW - 1) / NW;
+  static constexpr int S_PW = (S_TOT + NW - 1) / NW;
+  static constexpr int LOADS = A_PW + B_PW + S_PW;             // vm ops per wave per k-tile
+  static_assert(A_TOT >= 1 && B_TOT >= 1 && (!FP4 || S_TOT >= 1), "tile too small");
+  static_assert(LOADS * (NST - 2) < 64, "vmcnt range");
+  static_assert(STAGE % 16 == 0, "stage alignment");
+};
 
+// One output tile: rows [r0, r1) (r1 - r0 <= BM) of group g, columns [n0, n0 + BN).
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, int r0, int r1,
+                                          int n0) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  constexpr int CPR = C::CPR, NW = C::NW;
+  constexpr int WM = BM / WGM, WN = BN / WGN;      // wavefront tile
+  constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA blocks per wavefront
+  constexpr int S_PW1 = C::S_PW > 0 ? C::S_PW : 1;
+  constexpr int S_TOT1 = C::S_TOT > 0 ? C::S_TOT : 1;
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int nk = p.K / BK;
+
+  // the previous tile's stores must not be counted as in-flight loads below
+  wait_vm<0>();
+
+  // ---- per-lane global offsets of this lane's chunks (32-bit, from uniform bases)
+  const uint16_t* Abase = (const uint16_t*)p.A;
+  uint32_t aoff[C::A_PW];
+#pragma unroll
+  for (int j = 0; j < C::A_PW; ++j) {
+    const int blk = (wave + j * NW) % C::A_TOT;
+    const int q = blk * 64 + lane;                 // LDS chunk index in the A region
+    const int row = q / CPR, pos = q % CPR;
+    const int lr = min(r0 + row, r1 - 1);          // rows past the end re-read the last row
+    const uint32_t pr = p.a_rows ? (uint32_t)p.a_rows[lr] : (uint32_t)lr;
+    aoff[j] = pr * (uint32_t)p.lda + swz_chunk<CPR>(row, pos) * 8;
+  }
+  const char* Bbase = FP4 ? (const char*)p.B + (int64_t)g * p.b_gstride
+                          : (const char*)((const uint16_t*)p.B + (int64_t)g * p.b_gstride);
+  const char* Sbase = FP4 ? (const char*)p.b_scale + (int64_t)g * p.s_gstride : nullptr;
+  uint32_t boff[C::B_PW], soff[S_PW1];
+#pragma unroll
+  for (int j = 0; j < C::B_PW; ++j) {
+    const int blk = (wave + j * NW) % C::B_TOT;
+    if (FP4) {                                     // BK/32 chunks of codes per row, unswizzled
+      constexpr int QPR = BK / 32;
+      const int q = blk * 64 + lane, row = q / QPR, pos = q % QPR;
+      const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
+      boff[j] = n * (uint32_t)p.ldb + pos * 16;    // bytes
+    } else {
+      const int q = blk * 64 + lane, row = q / CPR, pos = q % CPR;
+      const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
+      boff[j] = n * (uint32_t)p.ldb + swz_chunk<CPR>(row, pos) * 8;   // elements
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < S_PW1; ++j) {
+    const int blk = (wave + j * NW) % S_TOT1;
+    const uint32_t n = (uint32_t)min(n0 + blk * 64 + lane, p.N - 1);
+    soff[j] = n * (uint32_t)p.lds_scale;           // bytes; BK/16 scale bytes per row per k-tile
+  }
+
+  // ---- issue the direct-to-LDS loads of k-tile kt into stage st
+#define MOE_ISSUE(KT, ST)                                                                     \
+  do {                                                                                        \
+    char* S_ = smem + (ST) * C::STAGE;                                                        \
+    const uint32_t k0_ = (uint32_t)(KT) * BK;                                                 \
+    _Pragma("unroll") for (int j = 0; j < C::A_PW; ++j) {                                     \
+      const int blk = (wave + j * NW) % C::A_TOT;                                             \
+      dma16(Abase + (aoff[j] + k0_), S_ + blk * 1024);                                        \
+    }                                                                                         \
+    if (FP4) {                                                                                \
+      _Pragma("unroll") for (int j = 0; j < C::B_PW; ++j) {                                   \
+        const int blk = (wave + j * NW) % C::B_TOT;                                           \
+        dma16(Bbase + (boff[j] + k0_ / 2), S_ + C::A_BYTES + blk * 1024);                     \
+      }                                                                                       \
+      _Pragma("unroll") for (int j = 0; j < C::S_PW; ++j) {                                   \
+        const int blk = (wave + j * NW) % S_TOT1;                                             \
+        dma4(Sbase + (soff[j] + k0_ / 16), S_ + C::A_BYTES + C::BQ_BYTES + blk * 256);        \
+      }                                                                                       \
+    } else {                                                                                  \
+      const int seg_ = (int)(k0_ / (uint32_t)p.kseg);                                         \
+      const uint16_t* Bk_ = (const uint16_t*)Bbase + (int64_t)seg_ * p.b_segstride +          \
+                            (k0_ - (uint32_t)seg_ * p.kseg);                                  \
+      _Pragma("unroll") for (int j = 0; j < C::B_PW; ++j) {                                   \
+        const int blk = (wave + j * NW) % C::B_TOT;                                           \
+        dma16(Bk_ + boff[j], S_ + C::A_BYTES + blk * 1024);                                   \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) MOE_ISSUE(s, s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wavefront's loads of k-tile kt are done once at most `pending` later
+    // k-tiles' loads remain in flight (loads complete in issue order)
+    const int pending = min(nk - 1 - kt, NST - 2);
+    if (NST >= 4 && pending >= 2) wait_vm<(NST >= 4 ? 2 : 0) * C::LOADS>();
+    else if (pending >= 1) wait_vm<C::LOADS>();
+    else wait_vm<0>();
+    bar();                                          // stage kt % NST complete for all waves
+    if (kt + NST - 1 < nk) MOE_ISSUE(kt + NST - 1, (kt + NST - 1) % NST);
+    const char* S = smem + (kt % NST) * C::STAGE;
+    const uint4* As = reinterpret_cast<const uint4*>(S);
+    const uint4* Bs;
+    if (FP4) {
+      // decode this k-tile's NVFP4 codes once into bf16 (buffer kt & 1)
+      uint4* D = reinterpret_cast<uint4*>(smem + NST * C::STAGE + (kt & 1) * C::BDQ);
+      const uint8_t* Q = reinterpret_cast<const uint8_t*>(S + C::A_BYTES);
+      const uint8_t* Sc = Q + C::BQ_BYTES;
+      constexpr int UNITS = BN * BK / 32;           // 32 codes (16 bytes) per unit
+#pragma unroll
+      for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
+        const int u = u0 + tid;
+        if (UNITS % C::NT == 0 || u < UNITS) {
+          const int row = u / (BK / 32), part = u % (BK / 32);
+          const uint4 q = *reinterpret_cast<const uint4*>(Q + row * (BK / 2) + part * 16);
+          const uint32_t sw = *reinterpret_cast<const uint32_t*>(Sc + row * (BK / 16));
+          const int sb = part * 2;                  // scale byte of this unit's first block
+          const float s0 = e4m3_to_f32((sw >> (8 * sb)) & 0xFFu);
+          const float s1 = e4m3_to_f32((sw >> (8 * (sb + 1))) & 0xFFu);
+          uint4 o0, o1, o2, o3;
+          dequant16(q.x, q.y, s0, o0, o1);
+          dequant16(q.z, q.w, s1, o2, o3);
+          const int c0 = part * 4;
+          D[row * CPR + swz_chunk<CPR>(row, c0 + 0)] = o0;
+          D[row * CPR + swz_chunk<CPR>(row, c0 + 1)] = o1;
+          D[row * CPR + swz_chunk<CPR>(row, c0 + 2)] = o2;
+          D[row * CPR + swz_chunk<CPR>(row, c0 + 3)] = o3;
+        }
+      }
+      bar_lds();
+      Bs = D;
+    } else {
+      Bs = reinterpret_cast<const uint4*>(S + C::A_BYTES);
+    }
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int ch = s * 2 + (lane >> 5);
+      bf16x8 a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WM + i * 32 + (lane & 31);
+        a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = wn * WN + j * 32 + (lane & 31);
+        b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+    }
+  }
+#undef MOE_ISSUE
+  bar_lds();   // every wave is done with the stages before the next tile's loads land
+
+  // epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
+  // col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
+  const float gs = (FP4 && p.b_gscale) ? p.b_gscale[g] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = r0 + wm * WM + i * 32 + (lane & 31);
+    if (row >= r1) continue;
+    float rsc = gs;
+    if (EPI == EPI_GATE_BF16) rsc *= p.row_scale[row];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= p.N) continue;
+        float v0 = acc[j][i][4 * q + 0], v1 = acc[j][i][4 * q + 1];
+        float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
+        const int64_t o = (int64_t)row * p.ldc + col;
+        if (EPI == EPI_SQRELU_BF16) {
+          v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
+          v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
+          v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
+        } else {
+          v0 *= rsc; v1 *= rsc; v2 *= rsc; v3 *= rsc;
+        }
+        if (EPI == EPI_F32) {
+          *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
+        } else if (EPI == EPI_Z) {
+          *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
+          *reinterpret_cast<uint2*>((uint16_t*)p.C2 + (int64_t)row * p.ldc2 + col) =
+              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+        } else {
+          if (EPI == EPI_BF16_ADD) {
+            const float4 ad = *reinterpret_cast<const float4*>(p.add + (int64_t)row * p.ld_add + col);
+            v0 += ad.x; v1 += ad.y; v2 += ad.z; v3 += ad.w;
+          }
+          *reinterpret_cast<uint2*>((uint16_t*)p.C + o) =
+              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+        }
+      }
+    }
+  }
+}
+
+// Persistent kernel over (row tile, column tile) items.  List 0 holds row tiles
+// of height <= BM (p.tiles / n_tiles[0], or the dense row blocks); list 1, when
+// BMS > 0, holds row tiles of height <= BMS (p.tiles2 / n_tiles[1]): the
+// remainders of each expert's rows, processed with a shorter tile.
+template <int BM, int BN, int BMS, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
+  extern __shared__ uint4 smem_u4[];
+  char* smem = reinterpret_cast<char*>(smem_u4);
+  const int ntn = (p.N + BN - 1) / BN;
+  const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
+  const int nrt1 = BMS > 0 ? p.n_tiles[1] : 0;
+  const int items0 = nrt0 * ntn;
+  const int total = items0 + nrt1 * ntn;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int rt = item / ntn, nt = item - rt * ntn;
+    int it = item;
+    const int4* list = p.tiles;
+    if (it >= items0) { it -= items0; list = p.tiles2; }
+    const int rt = it / ntn, nt = it - rt * ntn;
     int g = 0, r0, r1;
-    if (p.tiles) {
-      const int4 tl = p.tiles[rt];
+    if (list) {
+      const int4 tl = list[rt];
       g = tl.x; r0 = tl.y; r1 = tl.z;
     } else {
       r0 = rt * BM; r1 = min(p.M, r0 + BM);
     }
-    const int n0 = nt * BN;
-
-    // per-thread global sources
-    const uint16_t* asrc[A_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * 256, r = c >> 3, ch = c & 7;
-      const int lr = min(r0 + r, r1 - 1);
-      const int64_t pr = p.a_rows ? (int64_t)p.a_rows[lr] : (int64_t)lr;
-      asrc[i] = (const uint16_t*)p.A + pr * p.lda + ch * 8;
-    }
-    const uint8_t* bsrc[B_CH];
-    const uint8_t* ssrc[B_CH];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * 256;
-      if (FP4) {
-        const int r = c >> 1, half = c & 1;
-        const int n = min(n0 + r, p.N - 1);
-        bsrc[i] = (const uint8_t*)p.B + (int64_t)g * p.b_gstride + (int64_t)n * p.ldb + half * 16;
-        ssrc[i] = p.b_scale + (int64_t)g * p.s_gstride + (int64_t)n * p.lds_scale + half * 2;
-      } else {
-        const int r = c >> 3, ch = c & 7;
-        const int n = min(n0 + r, p.N - 1);
-        bsrc[i] = (const uint8_t*)((const uint16_t*)p.B + (int64_t)g * p.b_gstride +
-                                   (int64_t)n * p.ldb + ch * 8);
-        ssrc[i] = nullptr;
-      }
-    }
-
-    uint4 ra[A_CH], rb[B_CH];
-    uint32_t rs[B_CH];
-    auto load = [&](int kt) {
-      const int k0 = kt * 64;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(asrc[i] + k0);
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        if (FP4) {
-          rb[i] = *reinterpret_cast<const uint4*>(bsrc[i] + k0 / 2);
-          rs[i] = *reinterpret_cast<const uint16_t*>(ssrc[i] + k0 / 16);
-        } else {
-          const int seg = k0 / p.kseg, kin = k0 - seg * p.kseg;
-          rb[i] = *reinterpret_cast<const uint4*>(
-              (const uint16_t*)bsrc[i] + (int64_t)seg * p.b_segstride + kin);
-        }
-      }
-    };
-    auto store = [&](int buf) {
-      uint4* As = smem[buf];
-      uint4* Bs = smem[buf] + BM * 8;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * 256, r = c >> 3, ch = c & 7;
-        As[swz(r, ch)] = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * 256;
-        if (FP4) {
-          const int r = c >> 1, half = c & 1;
-          const float s0 = e4m3_to_f32(rs[i] & 0xFFu), s1 = e4m3_to_f32((rs[i] >> 8) & 0xFFu);
-          uint4 o0, o1, o2, o3;
-          dequant16(rb[i].x, rb[i].y, s0, o0, o1);
-          dequant16(rb[i].z, rb[i].w, s1, o2, o3);
-          Bs[swz(r, half * 4 + 0)] = o0;
-          Bs[swz(r, half * 4 + 1)] = o1;
-          Bs[swz(r, half * 4 + 2)] = o2;
-          Bs[swz(r, half * 4 + 3)] = o3;
-        } else {
-          const int r = c >> 3, ch = c & 7;
-          Bs[swz(r, ch)] = rb[i];
-        }
-      }
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) load(kt + 1);
-      const uint4* As = smem[cur];
-      const uint4* Bs = smem[cur] + BM * 8;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ch = s * 2 + (lane >> 5);
-        bf16x8 a[TM], b[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * (BM / 2) + i * 32 + (lane & 31);
-          a[i] = __builtin_bit_cast(bf16x8, As[swz(r, ch)]);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = wn * (BN / 2) + j * 32 + (lane & 31);
-          b[j] = __builtin_bit_cast(bf16x8, Bs[swz(n, ch)]);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) store(cur ^ 1);
-      __syncthreads();
-    }
-
-    // epilogue: D[i = 8*(r/4) + 4*(lane/32) + r%4][j = lane%32] of each 32x32 block
-    const float gs = (FP4 && p.b_gscale) ? p.b_gscale[g] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= r1) continue;
-        float rsc = 1.0f;
-        if (EPI == EPI_GATE_BF16) rsc = p.row_scale[row];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
-          if (col >= p.N) continue;
-          const float v = acc[i][j][r] * gs;
-          const int64_t o = (int64_t)row * p.ldc + col;
-          if (EPI == EPI_BF16) {
-            ((uint16_t*)p.C)[o] = (uint16_t)f2bf(v);
-          } else if (EPI == EPI_Z) {
-            ((float*)p.C)[o] = v;
-            ((uint16_t*)p.C2)[(int64_t)row * p.ldc2 + col] = (uint16_t)f2bf(v);
-          } else if (EPI == EPI_SQRELU_BF16) {
-            const float h = fmaxf(v, 0.0f);
-            ((uint16_t*)p.C)[o] = (uint16_t)f2bf(h * h);
-          } else if (EPI == EPI_GATE_BF16) {
-            ((uint16_t*)p.C)[o] = (uint16_t)f2bf(rsc * v);
-          } else if (EPI == EPI_F32) {
-            ((float*)p.C)[o] = v;
-          } else if (EPI == EPI_BF16_ADD) {
-            ((uint16_t*)p.C)[o] = (uint16_t)f2bf(v + p.add[(int64_t)row * p.ld_add + col]);
-          }
-        }
-      }
+    if (BMS > 0 && item >= items0)
+      gemm_tile<(BMS > 0 ? BMS : 64), BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
+    else
+      gemm_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
   }
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int max_row_tiles,
-                            int grid_cap, hipStream_t s) {
-  constexpr int BN = 128;
-  const int ntn = (a.N + BN - 1) / BN;
-  const int nrt = a.tiles ? max_row_tiles : (a.M + bm - 1) / bm;
-  const int64_t total = (int64_t)nrt * ntn;
+namespace {
+
+template <int BM, int BN, int BMS, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
+  constexpr size_t lds = (size_t)TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::LDS;
+  static_assert(lds <= 160 * 1024, "LDS");
+  auto* kern = gemm_bf16_kernel<BM, BN, BMS, BK, WGM, WGN, NST, FP4, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, a);
+  return hipGetLastError();
+}
+
+// bf16 weights: BK = 32 with 4 stages; NVFP4 weights: BK = 64 with 3 stages
+// (codes + scales staged raw, decoded in LDS).
+template <int BM, int BN, int BMS, int WGM, int WGN>
+hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int grid, hipStream_t s) {
+  if (fp4) {
+    if constexpr (BN <= 128 && BMS != 0) {   // NVFP4 is used for the grouped expert GEMMs only
+      switch (epi) {
+        case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, 3, true, EPI_SQRELU_BF16>(a, grid, s);
+        case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, 3, true, EPI_GATE_BF16>(a, grid, s);
+        default: break;
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (epi) {
+    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_SQRELU_BF16>(a, grid, s);
+    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_GATE_BF16>(a, grid, s);
+    default: break;
+  }
+  if (BMS != 0) return hipErrorInvalidValue;     // dense epilogues have no tile lists
+  switch (epi) {
+    case EPI_BF16: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16>(a, grid, s);
+    case EPI_Z: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_Z>(a, grid, s);
+    case EPI_F32: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_F32>(a, grid, s);
+    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16_ADD>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// Tile shapes: 256x256 (8 wavefronts, 2x4), 256x128 and 128x128 (4 wavefronts,
+// 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height
+// bm, list 1 of height bms; max_items bounds the items for the grid size.
+hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
+                            int64_t max_items, int grid_cap, hipStream_t s) {
+  if (!a.tiles && bms != 0) return hipErrorInvalidValue;
+  const int64_t total = a.tiles ? max_items
+                                : (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   int grid = (int)(total < grid_cap ? total : grid_cap);
   if (grid < 1) grid = 1;
-  dim3 g(grid), b(256);
-  if (bm != 128) return hipErrorInvalidValue;
-#define MOE_BF16_CASE(FP4, E) hipLaunchKernelGGL((gemm_bf16_kernel<128, BN, FP4, E>), g, b, 0, s, a)
-  if (b_nvfp4) {
-    switch (epi) {
-      case EPI_SQRELU_BF16: MOE_BF16_CASE(true, EPI_SQRELU_BF16); break;
-      case EPI_GATE_BF16: MOE_BF16_CASE(true, EPI_GATE_BF16); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (epi) {
-      case EPI_BF16: MOE_BF16_CASE(false, EPI_BF16); break;
-      case EPI_Z: MOE_BF16_CASE(false, EPI_Z); break;
-      case EPI_SQRELU_BF16: MOE_BF16_CASE(false, EPI_SQRELU_BF16); break;
-      case EPI_GATE_BF16: MOE_BF16_CASE(false, EPI_GATE_BF16); break;
-      case EPI_F32: MOE_BF16_CASE(false, EPI_F32); break;
-      case EPI_BF16_ADD: MOE_BF16_CASE(false, EPI_BF16_ADD); break;
-      default: return hipErrorInvalidValue;
-    }
+  if (!a.tiles) {
+    if (bm == 256 && bn == 256) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, grid, s);
+    if (bm == 256 && bn == 128) return launch_shape<256, 128, 0, 2, 2>(a, b_nvfp4, epi, grid, s);
+    if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, grid, s);
+    return hipErrorInvalidValue;
   }
-#undef MOE_BF16_CASE
-  return hipGetLastError();
+  if (bm == 256 && bn == 256 && bms == 64) return launch_shape<256, 256, 64, 2, 4>(a, b_nvfp4, epi, grid, s);
+  if (bm == 256 && bn == 128 && bms == 64) return launch_shape<256, 128, 64, 2, 2>(a, b_nvfp4, epi, grid, s);
+  if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, grid, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

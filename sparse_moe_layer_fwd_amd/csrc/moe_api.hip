@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -29,9 +30,9 @@ struct moe_handle {
 
 namespace {
 
-constexpr int kTokensPerChunk = 64;   // routing chunk (histogram / scatter unit)
-constexpr int kPrefillBM = 128;       // grouped bf16 GEMM row-tile height
+constexpr int kTokensPerChunk = 32;   // routing chunk (histogram / scatter unit)
 constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
+constexpr int kSmallBM = 64;          // grouped bf16 GEMM: height of each expert's remainder tiles
 constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -87,9 +88,9 @@ struct StageScope {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
-  size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, ntiles;
+  size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
   size_t slot_token, slot_gate, tk_slot, H, O, u, Hs, ys, total;
-  int nchunks, bm, max_row_tiles;
+  int nchunks, bm, bms, max_tiles, max_tiles2;
   bool f32, skinny;
 };
 
@@ -108,8 +109,19 @@ Plan make_plan(const moe_config_t& c, int T) {
   p.skinny = use_skinny(c, T);
   const size_t es = p.f32 ? 4 : 2;
   p.nchunks = (T + kTokensPerChunk - 1) / kTokensPerChunk;
-  p.bm = p.f32 ? kF32BM : kPrefillBM;
-  p.max_row_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
+  if (p.f32) {
+    p.bm = kF32BM;
+    p.bms = 0;
+    p.max_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
+    p.max_tiles2 = 0;
+  } else {
+    // full tiles of 256 rows when experts average >= 256 rows, else 128; the
+    // rows left over in each expert go to 64-row tiles
+    p.bm = (Tz * K >= 256 * N) ? 256 : 128;
+    p.bms = kSmallBM;
+    p.max_tiles = (int)((Tz * K) / p.bm);
+    p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
+  }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
   p.z32 = take(c.has_latent_proj ? Tz * L * 4 : 0);
@@ -121,8 +133,9 @@ Plan make_plan(const moe_config_t& c, int T) {
   p.cbase = take((size_t)p.nchunks * N * 4);
   p.counts = take(N * 4);
   p.offs = take((N + 1) * 4);
-  p.tiles = take((size_t)p.max_row_tiles * 16);
-  p.ntiles = take(4);
+  p.tiles = take((size_t)p.max_tiles * 16);
+  p.tiles2 = take((size_t)p.max_tiles2 * 16);
+  p.ntiles = take(8);
   p.slot_token = take(Tz * K * 4);
   p.slot_gate = take(Tz * K * 4);
   p.tk_slot = take(Tz * K * 4);
@@ -137,6 +150,20 @@ Plan make_plan(const moe_config_t& c, int T) {
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>((char*)ws + off); }
+
+// Dense bf16 GEMM tile shape: the largest tile that still gives every CU work.
+void dense_shape(int M, int N, int num_cu, int* bm, int* bn) {
+  auto tiles = [&](int a, int b) { return (int64_t)((M + a - 1) / a) * ((N + b - 1) / b); };
+  if (tiles(256, 256) >= num_cu) { *bm = 256; *bn = 256; }
+  else if (tiles(256, 128) >= num_cu) { *bm = 256; *bn = 128; }
+  else { *bm = 128; *bn = 128; }
+}
+
+hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, hipStream_t s) {
+  int bm, bn;
+  dense_shape(a.M, a.N, num_cu, &bm, &bn);
+  return launch_gemm_bf16(a, false, epi, bm, bn, 0, 0, num_cu * 2, s);
+}
 
 GemmArgs gemm_args() {
   GemmArgs a;
@@ -177,7 +204,7 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
       MOE_TRY(launch_gemm_f32(a, false, EPI_F32, cap, s));
     } else {
       a.C2 = at<void>(ws, p.z16); a.ldc2 = c.latent;
-      MOE_TRY(launch_gemm_bf16(a, false, EPI_Z, kPrefillBM, 0, cap, s));
+      MOE_TRY(dense_bf16(a, EPI_Z, h->num_cu, s));
     }
   }
   {
@@ -198,9 +225,9 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
                         at<int>(ws, p.idx), at<float>(ws, p.gate), at<int>(ws, p.ccount), s));
   }
   StageScope sc(MOE_STAGE_SCAN, s);
-  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, at<int>(ws, p.cbase),
-                      at<int>(ws, p.counts), at<int>(ws, p.offs), at<int4>(ws, p.tiles),
-                      at<int>(ws, p.ntiles), s));
+  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, p.bms,
+                      at<int>(ws, p.cbase), at<int>(ws, p.counts), at<int>(ws, p.offs),
+                      at<int4>(ws, p.tiles), at<int4>(ws, p.tiles2), at<int>(ws, p.ntiles), s));
   return MOE_OK;
 }
 
@@ -253,14 +280,20 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   a.b_gscale = G;
   a.N = (int)rows; a.K = (int)kdim;
   a.tiles = at<int4>(ws, p.tiles); a.n_tiles = at<int>(ws, p.ntiles);
+  a.tiles2 = at<int4>(ws, p.tiles2);
   a.C = C; a.ldc = rows;
   a.row_scale = at<float>(ws, p.slot_gate);
   if (p.f32) {
-    a.M = p.max_row_tiles;   // grouped: upper bound on row tiles (grid sizing)
+    a.M = p.max_tiles;   // grouped: upper bound on row tiles (grid sizing)
     MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_GATE_F32, cap, s));
   } else {
-    MOE_TRY(launch_gemm_bf16(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, kPrefillBM,
-                             p.max_row_tiles, cap, s));
+    // 256x256 (8 wavefronts) for bf16 weights; NVFP4 decode needs the registers
+    // of a 4-wavefront 256x128 tile
+    const int bn = (p.bm == 256 && !fp4) ? 256 : 128;
+    const int64_t ntn = (rows + bn - 1) / bn;
+    const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
+    MOE_TRY(launch_gemm_bf16(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, p.bm, bn, p.bms,
+                             items, h->num_cu, s));
   }
   return MOE_OK;
 }
@@ -437,7 +470,7 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     a.M = T; a.N = sm; a.K = c.d;
     a.C = at<void>(ws, p.Hs); a.ldc = sm;
     if (p.f32) MOE_TRY(launch_gemm_f32(a, false, EPI_SQRELU_F32, cap, s));
-    else MOE_TRY(launch_gemm_bf16(a, false, EPI_SQRELU_BF16, kPrefillBM, 0, cap, s));
+    else MOE_TRY(dense_bf16(a, EPI_SQRELU_BF16, h->num_cu, s));
     GemmArgs b = gemm_args();
     b.A = at<void>(ws, p.Hs); b.lda = sm;
     b.B = w.ws2; b.ldb = c.shared_ffn;
@@ -445,7 +478,7 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     b.M = T; b.N = c.d; b.K = sm;
     b.C = at<float>(ws, p.ys); b.ldc = c.d;
     if (p.f32) MOE_TRY(launch_gemm_f32(b, false, EPI_F32, cap, s));
-    else MOE_TRY(launch_gemm_bf16(b, false, EPI_F32, kPrefillBM, 0, cap, s));
+    else MOE_TRY(dense_bf16(b, EPI_F32, h->num_cu, s));
     ys = at<float>(ws, p.ys);
   }
   if (c.has_latent_proj) {
@@ -462,7 +495,7 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     a.C = y; a.ldc = c.d;
     a.add = ys; a.ld_add = c.d;
     if (p.f32) MOE_TRY(launch_gemm_f32(a, false, ys ? EPI_F32_ADD : EPI_F32, cap, s));
-    else MOE_TRY(launch_gemm_bf16(a, false, ys ? EPI_BF16_ADD : EPI_BF16, kPrefillBM, 0, cap, s));
+    else MOE_TRY(dense_bf16(a, ys ? EPI_BF16_ADD : EPI_BF16, h->num_cu, s));
   } else {
     StageScope sc(MOE_STAGE_COMBINE, s);
     MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot), T, c.top_k,

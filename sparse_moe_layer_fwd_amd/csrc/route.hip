@@ -25,13 +25,33 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 __device__ __forceinline__ uint32_t key_expert(uint64_t k) {
   return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
 }
+// One DPP step of a 64-bit max: combine with the value of another lane of the
+// same row (quad permutations and row rotations have no memory round-trip).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Wave-wide max: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror 4, row_ror 8
+// leave every lane with its 16-lane row's max; the four row maxima are then read
+// as scalars.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xB1>(v);
+  v = dpp_max_step<0x4E>(v);
+  v = dpp_max_step<0x124>(v);
+  v = dpp_max_step<0x128>(v);
+  const uint64_t a = readlane64(v, 0), b = readlane64(v, 16);
+  const uint64_t c = readlane64(v, 32), d = readlane64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
 // One block per chunk of `tc` tokens; one wavefront per token.  Each lane holds
@@ -119,18 +139,33 @@ __device__ int block_excl_scan_1024(int v, int* total_out) {
 }
 
 // Single block: per-expert totals over chunks (chunk_base = exclusive prefix
-// over chunks), expert offsets, and the row-tile list of height bm.
+// over chunks), expert offsets, and the grouped-GEMM row-tile lists.  With
+// bms == 0 every expert's rows are cut into tiles of height bm (list 0).  With
+// bms > 0 list 0 holds only full tiles of height bm and list 1 covers each
+// expert's remaining rows with tiles of height bms.  n_tiles[0..1] = list sizes.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_counts,
-                                                    int nchunks, int N, int bm,
+                                                    int nchunks, int N, int bm, int bms,
                                                     int* __restrict__ chunk_base,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offs,
                                                     int4* __restrict__ tiles,
+                                                    int4* __restrict__ tiles2,
                                                     int* __restrict__ n_tiles) {
   const int e = threadIdx.x;
   int total = 0;
   if (e < N) {
-    for (int c = 0; c < nchunks; ++c) {
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8) {            // 8 independent loads in flight
+      int v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = chunk_counts[(int64_t)(c + i) * N + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        chunk_base[(int64_t)(c + i) * N + e] = total;
+        total += v[i];
+      }
+    }
+    for (; c < nchunks; ++c) {
       const int v = chunk_counts[(int64_t)c * N + e];
       chunk_base[(int64_t)c * N + e] = total;
       total += v;
@@ -138,23 +173,33 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   }
   int all = 0;
   const int off = block_excl_scan_1024(total, &all);
-  const int nt = bm > 0 ? (total + bm - 1) / bm : 0;
-  int all_tiles = 0;
-  const int toff = block_excl_scan_1024(nt, &all_tiles);
+  const int nbig = bms > 0 ? total / bm : (total + bm - 1) / bm;
+  const int rem = bms > 0 ? total - nbig * bm : 0;
+  const int nsmall = bms > 0 ? (rem + bms - 1) / bms : 0;
+  int all_big = 0, all_small = 0;
+  const int toff = block_excl_scan_1024(nbig, &all_big);
+  const int soff = block_excl_scan_1024(nsmall, &all_small);
   if (e < N) {
     counts[e] = total;
     offs[e] = off;
     if (e == N - 1) offs[N] = off + total;
-    for (int i = 0; i < nt; ++i)
+    for (int i = 0; i < nbig; ++i)
       tiles[toff + i] = make_int4(e, off + i * bm, min(off + total, off + (i + 1) * bm), 0);
+    const int base = off + nbig * bm;
+    for (int i = 0; i < nsmall; ++i)
+      tiles2[soff + i] = make_int4(e, base + i * bms, min(off + total, base + (i + 1) * bms), 0);
   }
-  if (e == 0) n_tiles[0] = all_tiles;
+  if (e == 0) {
+    n_tiles[0] = all_big;
+    n_tiles[1] = all_small;
+  }
 }
 
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int* chunk_base,
-                       int* counts, int* offs, int4* tiles, int* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm,
-                     chunk_base, counts, offs, tiles, n_tiles);
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int* chunk_base,
+                       int* counts, int* offs, int4* tiles, int4* tiles2, int* n_tiles,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm, bms,
+                     chunk_base, counts, offs, tiles, tiles2, n_tiles);
   return hipGetLastError();
 }
 
