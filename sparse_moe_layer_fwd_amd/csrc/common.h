@@ -81,8 +81,9 @@ struct SkinnyArgs {
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s);
+// num_cu: compute units of the device (the persistent grid is sized from it)
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
-                            int64_t max_items, int grid_cap, hipStream_t s);
+                            int64_t max_items, int num_cu, hipStream_t s);
 hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);

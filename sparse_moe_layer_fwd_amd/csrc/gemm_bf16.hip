@@ -37,7 +37,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
+// 4-byte direct load (sub-dword LDS-DMA forms are not used: their LDS placement
+// is not the 2- or 1-byte lane stride the packed layouts here would need)
+template <int BYTES>
+__device__ __forceinline__ void dma_small(const void* g, void* lds_wave_base) {
+  static_assert(BYTES == 4, "dword LDS-DMA only");
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
 }
 
@@ -58,23 +62,34 @@ __device__ __forceinline__ int swz_chunk(int row, int c) {
   return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
 }
 
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t byte, float s) {
-  const float lo = e2m1_to_f32(byte & 15u) * s;
-  const float hi = e2m1_to_f32((byte >> 4) & 15u) * s;
-  // exact products: the bf16 value is the upper half of the fp32 one
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+// NVFP4 decode with the gfx950 conversion v_cvt_scalef32_pk_bf16_fp4, which
+// turns one byte (two E2M1 codes, low nibble first) into two bf16 multiplied by
+// the power of two in its scale operand (only the scale's exponent is used).
+// The E4M3 block scale s = 2^E * f is applied as 2^E in the conversion and f
+// (a 4-bit significand with s's sign) as one fp32 multiply; both steps are
+// exact because every e2m1 * e4m3 product fits in bf16.
+struct Fp4Scale {
+  float pow2, frac;
+};
+__device__ __forceinline__ Fp4Scale split_scale(uint32_t e4m3) {
+  const float s = e4m3_to_f32(e4m3);
+  const uint32_t b = __float_as_uint(s);
+  Fp4Scale r;
+  r.pow2 = __uint_as_float(b & 0x7F800000u);
+  r.frac = s == 0.0f ? 0.0f : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+  return r;
 }
-
-// 16 packed codes (8 bytes in two words) of one block with scale s -> 16 bf16
-__device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, float s, uint4& o0, uint4& o1) {
-  o0.x = fp4x2_to_bf16x2(w0 & 0xFFu, s);
-  o0.y = fp4x2_to_bf16x2((w0 >> 8) & 0xFFu, s);
-  o0.z = fp4x2_to_bf16x2((w0 >> 16) & 0xFFu, s);
-  o0.w = fp4x2_to_bf16x2(w0 >> 24, s);
-  o1.x = fp4x2_to_bf16x2(w1 & 0xFFu, s);
-  o1.y = fp4x2_to_bf16x2((w1 >> 8) & 0xFFu, s);
-  o1.z = fp4x2_to_bf16x2((w1 >> 16) & 0xFFu, s);
-  o1.w = fp4x2_to_bf16x2(w1 >> 24, s);
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, const Fp4Scale& sc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.pow2, BYTE));
+  const float lo = __uint_as_float(pr << 16) * sc.frac;
+  const float hi = __uint_as_float(pr & 0xFFFF0000u) * sc.frac;
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+// 8 codes (one dword) -> 8 bf16 (one uint4)
+__device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
+  return make_uint4(fp4_pair<0>(w, sc), fp4_pair<1>(w, sc), fp4_pair<2>(w, sc), fp4_pair<3>(w, sc));
 }
 
 }  // namespace
@@ -85,14 +100,14 @@ struct TileCfg {
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per bf16 row
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int BQ_BYTES = BN * BK / 2;                 // NVFP4 codes
-  static constexpr int BS_BYTES = BN * BK / 16;                // NVFP4 scales
+  static constexpr int BS_BYTES = BN * 4;                      // NVFP4 scales: one aligned dword per row
   static constexpr int B_BYTES = FP4 ? BQ_BYTES + BS_BYTES : BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int BDQ = FP4 ? BN * BK * 2 : 0;            // decoded B (double-buffered)
   static constexpr int LDS = NST * STAGE + 2 * BDQ;
   static constexpr int A_TOT = BM * CPR / 64;                  // 1 KB DMA blocks per k-tile
   static constexpr int B_TOT = FP4 ? BQ_BYTES / 1024 : BN * CPR / 64;
-  static constexpr int S_TOT = FP4 ? BS_BYTES / 256 : 0;       // 4-byte-per-lane blocks
+  static constexpr int S_TOT = FP4 ? BS_BYTES / 256 : 0;       // dword-per-lane DMA blocks
   static constexpr int A_PW = (A_TOT + NW - 1) / NW;           // per wavefront
   static constexpr int B_PW = (B_TOT + NW - 1) / NW;
   static constexpr int S_PW = (S_TOT + NW - 1) / NW;
@@ -154,7 +169,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
   for (int j = 0; j < S_PW1; ++j) {
     const int blk = (wave + j * NW) % S_TOT1;
     const uint32_t n = (uint32_t)min(n0 + blk * 64 + lane, p.N - 1);
-    soff[j] = n * (uint32_t)p.lds_scale;           // bytes; BK/16 scale bytes per row per k-tile
+    soff[j] = n * (uint32_t)p.lds_scale;           // bytes; the k-tile's BK/16 scale bytes sit in
+                                                   // the aligned dword loaded per row
   }
 
   // ---- issue the direct-to-LDS loads of k-tile kt into stage st
@@ -173,7 +189,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
       }                                                                                       \
       _Pragma("unroll") for (int j = 0; j < C::S_PW; ++j) {                                   \
         const int blk = (wave + j * NW) % S_TOT1;                                             \
-        dma4(Sbase + (soff[j] + k0_ / 16), S_ + C::A_BYTES + C::BQ_BYTES + blk * 256);        \
+        dma_small<4>(Sbase + ((soff[j] + k0_ / 16) & ~3u), S_ + C::A_BYTES + C::BQ_BYTES + blk * 256); \
       }                                                                                       \
     } else {                                                                                  \
       const int seg_ = (int)(k0_ / (uint32_t)p.kseg);                                         \
@@ -194,53 +210,56 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
+  // ---- NVFP4: decode raw k-tile KT (stage KT % NST) into bf16 buffer KT & 1
+#define MOE_DECODE(KT)                                                                        \
+  do {                                                                                        \
+    const char* S_ = smem + ((KT) % NST) * C::STAGE;                                          \
+    uint4* D_ = reinterpret_cast<uint4*>(smem + NST * C::STAGE + ((KT) & 1) * C::BDQ);         \
+    const uint8_t* Q_ = reinterpret_cast<const uint8_t*>(S_ + C::A_BYTES);                    \
+    const uint8_t* Sc_ = Q_ + C::BQ_BYTES;                                                    \
+    constexpr int UNITS = BN * BK / 16;             /* one 16-code block per unit */            \
+    _Pragma("unroll") for (int u0 = 0; u0 < UNITS; u0 += C::NT) {                             \
+      const int u = u0 + tid;                                                                 \
+      if (UNITS % C::NT == 0 || u < UNITS) {                                                  \
+        const int row = u / (BK / 16), blk = u % (BK / 16);                                   \
+        const uint2 q = *reinterpret_cast<const uint2*>(Q_ + row * (BK / 2) + blk * 8);       \
+        const Fp4Scale sc = split_scale(Sc_[row * 4 + (((KT) * (BK / 16)) & 3) + blk]);       \
+        D_[row * CPR + swz_chunk<CPR>(row, 2 * blk + 0)] = fp4x8(q.x, sc);                    \
+        D_[row * CPR + swz_chunk<CPR>(row, 2 * blk + 1)] = fp4x8(q.y, sc);                    \
+      }                                                                                       \
+    }                                                                                         \
+  } while (0)
+  // wait until this wavefront's loads of some k-tile are done, given that at
+  // most `pending` later k-tiles' loads may stay in flight (in-order completion)
+#define MOE_WAIT(PENDING)                                                                     \
+  do {                                                                                        \
+    const int pd_ = (PENDING);                                                                \
+    if (NST >= 4 && pd_ >= 2) wait_vm<(NST >= 4 ? 2 : 0) * C::LOADS>();                       \
+    else if (pd_ >= 1) wait_vm<C::LOADS>();                                                   \
+    else wait_vm<0>();                                                                        \
+  } while (0)
+
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < nk) MOE_ISSUE(s, s);
+  if (FP4) {                                        // decode k-tile 0 ahead of the loop
+    MOE_WAIT(min(nk - 1, NST - 2));
+    bar();
+    MOE_DECODE(0);
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
-    // this wavefront's loads of k-tile kt are done once at most `pending` later
-    // k-tiles' loads remain in flight (loads complete in issue order)
-    const int pending = min(nk - 1 - kt, NST - 2);
-    if (NST >= 4 && pending >= 2) wait_vm<(NST >= 4 ? 2 : 0) * C::LOADS>();
-    else if (pending >= 1) wait_vm<C::LOADS>();
-    else wait_vm<0>();
-    bar();                                          // stage kt % NST complete for all waves
+    // bf16: k-tile kt must have landed.  NVFP4: the raw codes of kt + 1 too,
+    // because they are decoded while k-tile kt is multiplied.
+    const int need = FP4 ? min(kt + 1, nk - 1) : kt;
+    MOE_WAIT(min(nk - 1 - need, NST - 2));
+    if (FP4) bar_lds(); else bar();                 // stages (and decoded B) complete for all waves
     if (kt + NST - 1 < nk) MOE_ISSUE(kt + NST - 1, (kt + NST - 1) % NST);
+    if (FP4 && kt + 1 < nk) MOE_DECODE(kt + 1);
     const char* S = smem + (kt % NST) * C::STAGE;
     const uint4* As = reinterpret_cast<const uint4*>(S);
-    const uint4* Bs;
-    if (FP4) {
-      // decode this k-tile's NVFP4 codes once into bf16 (buffer kt & 1)
-      uint4* D = reinterpret_cast<uint4*>(smem + NST * C::STAGE + (kt & 1) * C::BDQ);
-      const uint8_t* Q = reinterpret_cast<const uint8_t*>(S + C::A_BYTES);
-      const uint8_t* Sc = Q + C::BQ_BYTES;
-      constexpr int UNITS = BN * BK / 32;           // 32 codes (16 bytes) per unit
-#pragma unroll
-      for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
-        const int u = u0 + tid;
-        if (UNITS % C::NT == 0 || u < UNITS) {
-          const int row = u / (BK / 32), part = u % (BK / 32);
-          const uint4 q = *reinterpret_cast<const uint4*>(Q + row * (BK / 2) + part * 16);
-          const uint32_t sw = *reinterpret_cast<const uint32_t*>(Sc + row * (BK / 16));
-          const int sb = part * 2;                  // scale byte of this unit's first block
-          const float s0 = e4m3_to_f32((sw >> (8 * sb)) & 0xFFu);
-          const float s1 = e4m3_to_f32((sw >> (8 * (sb + 1))) & 0xFFu);
-          uint4 o0, o1, o2, o3;
-          dequant16(q.x, q.y, s0, o0, o1);
-          dequant16(q.z, q.w, s1, o2, o3);
-          const int c0 = part * 4;
-          D[row * CPR + swz_chunk<CPR>(row, c0 + 0)] = o0;
-          D[row * CPR + swz_chunk<CPR>(row, c0 + 1)] = o1;
-          D[row * CPR + swz_chunk<CPR>(row, c0 + 2)] = o2;
-          D[row * CPR + swz_chunk<CPR>(row, c0 + 3)] = o3;
-        }
-      }
-      bar_lds();
-      Bs = D;
-    } else {
-      Bs = reinterpret_cast<const uint4*>(S + C::A_BYTES);
-    }
+    const uint4* Bs = FP4 ? reinterpret_cast<const uint4*>(smem + NST * C::STAGE + (kt & 1) * C::BDQ)
+                          : reinterpret_cast<const uint4*>(S + C::A_BYTES);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int ch = s * 2 + (lane >> 5);
@@ -262,6 +281,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
     }
   }
+#undef MOE_DECODE
+#undef MOE_WAIT
 #undef MOE_ISSUE
   bar_lds();   // every wave is done with the stages before the next tile's loads land
 
@@ -322,7 +343,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   const int nrt1 = BMS > 0 ? p.n_tiles[1] : 0;
   const int items0 = nrt0 * ntn;
   const int total = items0 + nrt1 * ntn;
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // Consecutive items (the column tiles of one row tile, then the next row
+  // tiles of the same expert) go to blocks of the same XCD, which share an L2:
+  // block b runs on XCD b % 8, so it takes the items of slice b % 8 of each
+  // round of gridDim.x items.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = G >> 3;
+  const int base = (G & 7) == 0 ? xcd * per_xcd + slot : blockIdx.x;
+  for (int round = 0; round * G < total; ++round) {
+    const int item = round * G + base;
+    if (item >= total) continue;
     int it = item;
     const int4* list = p.tiles;
     if (it >= items0) { it -= items0; list = p.tiles2; }
@@ -344,7 +374,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
 namespace {
 
 template <int BM, int BN, int BMS, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
-hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
+hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t s) {
   constexpr size_t lds = (size_t)TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::LDS;
   static_assert(lds <= 160 * 1024, "LDS");
   auto* kern = gemm_bf16_kernel<BM, BN, BMS, BK, WGM, WGN, NST, FP4, EPI>;
@@ -355,35 +385,40 @@ hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  // persistent grid: as many blocks as fit at once (a multiple of the 8 XCDs)
+  const int per_cu = (int)((160 * 1024) / lds);
+  const int64_t cap = ((int64_t)num_cu * (per_cu > 0 ? per_cu : 1)) & ~7LL;
+  int grid = (int)(total < cap ? total : cap);
+  if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WGM * WGN), lds, s, a);
   return hipGetLastError();
 }
 
-// bf16 weights: BK = 32 with 4 stages; NVFP4 weights: BK = 64 with 3 stages
-// (codes + scales staged raw, decoded in LDS).
+// BK = 32 with a 4-stage ring; NVFP4 codes + scales are staged raw and decoded
+// in LDS one k-tile ahead of the MFMAs.
 template <int BM, int BN, int BMS, int WGM, int WGN>
-hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int grid, hipStream_t s) {
+hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int num_cu, hipStream_t s) {
   if (fp4) {
-    if constexpr (BN <= 128 && BMS != 0) {   // NVFP4 is used for the grouped expert GEMMs only
+    if constexpr (BMS != 0) {   // NVFP4 is used for the grouped expert GEMMs only
       switch (epi) {
-        case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, 3, true, EPI_SQRELU_BF16>(a, grid, s);
-        case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, 3, true, EPI_GATE_BF16>(a, grid, s);
+        case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_SQRELU_BF16>(a, grid, num_cu, s);
+        case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_GATE_BF16>(a, grid, num_cu, s);
         default: break;
       }
     }
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_SQRELU_BF16>(a, grid, s);
-    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_GATE_BF16>(a, grid, s);
+    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_SQRELU_BF16>(a, grid, num_cu, s);
+    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_GATE_BF16>(a, grid, num_cu, s);
     default: break;
   }
   if (BMS != 0) return hipErrorInvalidValue;     // dense epilogues have no tile lists
   switch (epi) {
-    case EPI_BF16: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16>(a, grid, s);
-    case EPI_Z: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_Z>(a, grid, s);
-    case EPI_F32: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_F32>(a, grid, s);
-    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16_ADD>(a, grid, s);
+    case EPI_BF16: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16>(a, grid, num_cu, s);
+    case EPI_Z: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_Z>(a, grid, num_cu, s);
+    case EPI_F32: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_F32>(a, grid, num_cu, s);
+    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16_ADD>(a, grid, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -394,21 +429,19 @@ hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int grid, hipStrea
 // 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height
 // bm, list 1 of height bms; max_items bounds the items for the grid size.
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
-                            int64_t max_items, int grid_cap, hipStream_t s) {
+                            int64_t max_items, int num_cu, hipStream_t s) {
   if (!a.tiles && bms != 0) return hipErrorInvalidValue;
   const int64_t total = a.tiles ? max_items
                                 : (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
-  int grid = (int)(total < grid_cap ? total : grid_cap);
-  if (grid < 1) grid = 1;
   if (!a.tiles) {
-    if (bm == 256 && bn == 256) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, grid, s);
-    if (bm == 256 && bn == 128) return launch_shape<256, 128, 0, 2, 2>(a, b_nvfp4, epi, grid, s);
-    if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, grid, s);
+    if (bm == 256 && bn == 256) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
+    if (bm == 256 && bn == 128) return launch_shape<256, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
+    if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
     return hipErrorInvalidValue;
   }
-  if (bm == 256 && bn == 256 && bms == 64) return launch_shape<256, 256, 64, 2, 4>(a, b_nvfp4, epi, grid, s);
-  if (bm == 256 && bn == 128 && bms == 64) return launch_shape<256, 128, 64, 2, 2>(a, b_nvfp4, epi, grid, s);
-  if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, grid, s);
+  if (bm == 256 && bn == 256 && bms == 64) return launch_shape<256, 256, 64, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
+  if (bm == 256 && bn == 128 && bms == 64) return launch_shape<256, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
+  if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
   return hipErrorInvalidValue;
 }
 

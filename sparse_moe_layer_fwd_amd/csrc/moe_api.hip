@@ -162,7 +162,7 @@ void dense_shape(int M, int N, int num_cu, int* bm, int* bn) {
 hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, hipStream_t s) {
   int bm, bn;
   dense_shape(a.M, a.N, num_cu, &bm, &bn);
-  return launch_gemm_bf16(a, false, epi, bm, bn, 0, 0, num_cu * 2, s);
+  return launch_gemm_bf16(a, false, epi, bm, bn, 0, 0, num_cu, s);
 }
 
 GemmArgs gemm_args() {
@@ -287,9 +287,7 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
     a.M = p.max_tiles;   // grouped: upper bound on row tiles (grid sizing)
     MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_GATE_F32, cap, s));
   } else {
-    // 256x256 (8 wavefronts) for bf16 weights; NVFP4 decode needs the registers
-    // of a 4-wavefront 256x128 tile
-    const int bn = (p.bm == 256 && !fp4) ? 256 : 128;
+    const int bn = p.bm == 256 ? 256 : 128;
     const int64_t ntn = (rows + bn - 1) / bn;
     const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
     MOE_TRY(launch_gemm_bf16(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, p.bm, bn, p.bms,
