@@ -192,9 +192,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
         dma_small<4>(Sbase + ((soff[j] + k0_ / 16) & ~3u), S_ + C::A_BYTES + C::BQ_BYTES + blk * 256); \
       }                                                                                       \
     } else {                                                                                  \
-      const int seg_ = (int)(k0_ / (uint32_t)p.kseg);                                         \
-      const uint16_t* Bk_ = (const uint16_t*)Bbase + (int64_t)seg_ * p.b_segstride +          \
-                            (k0_ - (uint32_t)seg_ * p.kseg);                                  \
+      const uint16_t* Bk_ = (const uint16_t*)Bbase + k0_;                                     \
+      if (p.kseg < p.K) {             /* B stored as k segments (shared experts' W2) */       \
+        const int seg_ = (int)(k0_ / (uint32_t)p.kseg);                                       \
+        Bk_ = (const uint16_t*)Bbase + (int64_t)seg_ * p.b_segstride +                        \
+              (k0_ - (uint32_t)seg_ * p.kseg);                                                \
+      }                                                                                       \
       _Pragma("unroll") for (int j = 0; j < C::B_PW; ++j) {                                   \
         const int blk = (wave + j * NW) % C::B_TOT;                                           \
         dma16(Bk_ + boff[j], S_ + C::A_BYTES + blk * 1024);                                   \
@@ -356,7 +359,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
     int it = item;
     const int4* list = p.tiles;
     if (it >= items0) { it -= items0; list = p.tiles2; }
-    const int rt = it / ntn, nt = it - rt * ntn;
+    int rt = it / ntn, nt = it - rt * ntn;
+    if (!list && ntn > 8) {
+      // dense and wide: walk bands of 4 row tiles column by column, so the 32
+      // consecutive items of one XCD reuse 4 A and 8 B strips from its L2
+      const int band = it / (4 * ntn), in = it - band * 4 * ntn;
+      const int rows = min(4, nrt0 - band * 4);
+      rt = band * 4 + in % rows;
+      nt = in / rows;
+    }
     int g = 0, r0, r1;
     if (list) {
       const int4 tl = list[rt];
@@ -364,10 +375,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
     } else {
       r0 = rt * BM; r1 = min(p.M, r0 + BM);
     }
-    if (BMS > 0 && item >= items0)
-      gemm_tile<(BMS > 0 ? BMS : 64), BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
-    else
-      gemm_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
+    if constexpr (BMS > 0) {
+      if (item >= items0) {
+        gemm_tile<BMS, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
+        continue;
+      }
+    }
+    gemm_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
   }
 }
 
@@ -394,10 +408,12 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
   return hipGetLastError();
 }
 
-// BK = 32 with a 4-stage ring; NVFP4 codes + scales are staged raw and decoded
-// in LDS one k-tile ahead of the MFMAs.
+// bf16: BK = 64 (fewer barriers per flop) with 2 stages for 256x256 tiles
+// and 3 for the smaller ones.  NVFP4: BK = 32 with a 4-stage ring; the codes and
+// scales are staged raw and decoded in LDS one k-tile ahead of the MFMAs.
 template <int BM, int BN, int BMS, int WGM, int WGN>
 hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int num_cu, hipStream_t s) {
+  constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
   if (fp4) {
     if constexpr (BMS != 0) {   // NVFP4 is used for the grouped expert GEMMs only
       switch (epi) {
@@ -409,16 +425,16 @@ hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int 
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_SQRELU_BF16>(a, grid, num_cu, s);
-    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, false, EPI_GATE_BF16>(a, grid, num_cu, s);
+    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, NSTB, false, EPI_SQRELU_BF16>(a, grid, num_cu, s);
+    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, NSTB, false, EPI_GATE_BF16>(a, grid, num_cu, s);
     default: break;
   }
   if (BMS != 0) return hipErrorInvalidValue;     // dense epilogues have no tile lists
   switch (epi) {
-    case EPI_BF16: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16>(a, grid, num_cu, s);
-    case EPI_Z: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_Z>(a, grid, num_cu, s);
-    case EPI_F32: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_F32>(a, grid, num_cu, s);
-    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 32, WGM, WGN, 4, false, EPI_BF16_ADD>(a, grid, num_cu, s);
+    case EPI_BF16: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_BF16>(a, grid, num_cu, s);
+    case EPI_Z: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_Z>(a, grid, num_cu, s);
+    case EPI_F32: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_F32>(a, grid, num_cu, s);
+    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_BF16_ADD>(a, grid, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }
