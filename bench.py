@@ -126,11 +126,11 @@ def main():
     n_dn, ms_dn = stages["expert_down"]
     launches = n_up + n_dn
     avg_ms = (ms_up + ms_dn) / max(1, launches)
+    # algorithmic work of one grouped launch: 2*T*K*l*m FLOP, and the weights of
+    # every touched expert (one matrix) read once; expert-sorted rows are
+    # intermediates of this implementation and are not counted
     flops_launch = 2.0 * cfg.T * cfg.top_k * cfg.latent * cfg.ffn
-    wbytes = touched * expert_weight_bytes_per_matrix(cfg)
-    act_es = 4 if cfg.act == "f32" else 2
-    act_bytes = cfg.T * cfg.top_k * (cfg.latent + cfg.ffn) * act_es   # rows in + rows out
-    bytes_launch = wbytes + act_bytes
+    bytes_launch = touched * expert_weight_bytes_per_matrix(cfg)
     peak_f = PEAK_F32_TFLOPS if cfg.expert == "f32" else PEAK_BF16_TFLOPS
     t_mfma = flops_launch / (peak_f * 1e12)
     t_hbm = bytes_launch / (PEAK_HBM_GBS * 1e9)

@@ -30,7 +30,7 @@ struct moe_handle {
 
 namespace {
 
-constexpr int kTokensPerChunk = 32;   // routing chunk (histogram / scatter unit)
+constexpr int kTokensPerChunk = 32;   // routing chunk: one histogram row / one scatter wavefront
 constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
 constexpr int kSmallBM = 64;          // grouped bf16 GEMM: height of each expert's remainder tiles
 constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path

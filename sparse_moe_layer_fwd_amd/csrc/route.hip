@@ -54,60 +54,62 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ab > cd ? ab : cd;
 }
 
-// One block per chunk of `tc` tokens; one wavefront per token.  Each lane holds
-// the logits of experts lane, lane+64, ...; K rounds of a wave-wide max over
-// packed (value, id) keys give the K largest in descending order.
+// Zero `n` ints (the chunk histograms) with plain stores: safe inside captured graphs.
+__global__ __launch_bounds__(256) void zero_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// One wavefront per token (4 per block).  Each lane holds the logits of experts
+// lane, lane+64, ...; K rounds of a wave-wide max over packed (value, id) keys
+// give the K largest in descending order.  The per-chunk expert histogram of
+// chunk t / tc is kept with integer atomics (order-independent results).
 template <int NJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int N,
                                                    int K, int tc, int* __restrict__ idx,
                                                    float* __restrict__ gate,
                                                    int* __restrict__ chunk_counts) {
-  __shared__ int hist[1024];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < N; i += 256) hist[i] = 0;
-  __syncthreads();
-  const int c = blockIdx.x;
-  const int t_end = min(T, (c + 1) * tc);
-  for (int t = c * tc + wave; t < t_end; t += 4) {
-    uint64_t key[NJ];
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  uint64_t key[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = j * 64 + lane;
-      key[j] = e < N ? make_key(logits[(int64_t)t * N + e], (uint32_t)e) : 0ull;
-    }
-    uint32_t taken = 0;
-    uint64_t mine = 0;
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = 0;
-      int bj = -1;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (!((taken >> j) & 1u) && key[j] > best) { best = key[j]; bj = j; }
-      const uint64_t w = wave_max_u64(best);
-      if (bj >= 0 && best == w) taken |= 1u << bj;
-      if (lane == k) mine = w;
-    }
-    const float v = key_value(mine);
-    const float vmax = __shfl(v, 0, 64);
-    float ex = lane < K ? expf(v - vmax) : 0.0f;
-    float s = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane < K) {
-      const uint32_t e = key_expert(mine);
-      idx[(int64_t)t * K + lane] = (int)e;
-      gate[(int64_t)t * K + lane] = ex / s;
-      atomicAdd(&hist[e], 1);
-    }
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * 64 + lane;
+    key[j] = e < N ? make_key(logits[(int64_t)t * N + e], (uint32_t)e) : 0ull;
   }
-  __syncthreads();
-  for (int i = tid; i < N; i += 256) chunk_counts[(int64_t)c * N + i] = hist[i];
+  uint32_t taken = 0;
+  uint64_t mine = 0;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = 0;
+    int bj = -1;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!((taken >> j) & 1u) && key[j] > best) { best = key[j]; bj = j; }
+    const uint64_t w = wave_max_u64(best);
+    if (bj >= 0 && best == w) taken |= 1u << bj;
+    if (lane == k) mine = w;
+  }
+  const float v = key_value(mine);
+  const float vmax = __shfl(v, 0, 64);
+  float ex = lane < K ? expf(v - vmax) : 0.0f;
+  float s = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane < K) {
+    const uint32_t e = key_expert(mine);
+    idx[(int64_t)t * K + lane] = (int)e;
+    gate[(int64_t)t * K + lane] = ex / s;
+    atomicAdd(&chunk_counts[(int64_t)(t / tc) * N + e], 1);
+  }
 }
 
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s) {
   const int nchunks = (T + tc - 1) / tc;
-  dim3 g(nchunks), b(256);
+  const int nz = nchunks * N;
+  hipLaunchKernelGGL(zero_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, chunk_counts, nz);
+  dim3 g((T + 3) / 4), b(256);
   if (N <= 64) hipLaunchKernelGGL(topk_kernel<1>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
   else if (N <= 128) hipLaunchKernelGGL(topk_kernel<2>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
   else if (N <= 256) hipLaunchKernelGGL(topk_kernel<4>, g, b, 0, s, logits, T, N, K, tc, idx, gate, chunk_counts);
@@ -203,8 +205,10 @@ hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int 
   return hipGetLastError();
 }
 
-// One wavefront per chunk; assignments (t, k) are visited in order, so within an
-// expert the slots follow (t, k) order: a stable, deterministic scatter.
+// One wavefront per chunk of tc tokens.  Tokens are visited in order; lane k
+// handles assignment (t, k).  A token's K experts are distinct, so the K lanes
+// update K different LDS counters: within an expert the slots follow (t, k)
+// order, a stable and deterministic scatter.
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx,
                                                      const float* __restrict__ gate, int T, int K,
                                                      int N, int tc,
@@ -217,24 +221,14 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx
   const int c = blockIdx.x, lane = threadIdx.x;
   for (int i = lane; i < N; i += 64) cnt[i] = offs[i] + chunk_base[(int64_t)c * N + i];
   __syncthreads();
-  const int64_t a0 = (int64_t)c * tc * K;
-  const int64_t a1 = (int64_t)min(T, (c + 1) * tc) * K;
-  for (int64_t base = a0; base < a1; base += 64) {
-    const int64_t a = base + lane;
-    const bool valid = a < a1;
-    const int e = valid ? idx[a] : -1;
-    int rank = 0, tot = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j, 64);
-      if (ej == e) { ++tot; if (j < lane) ++rank; }
-    }
-    const int slot = valid ? cnt[e] + rank : 0;
-    __syncthreads();
-    if (valid && rank == 0) cnt[e] += tot;
-    __syncthreads();
-    if (valid) {
-      slot_token[slot] = (int)(a / K);
+  const int t1 = min(T, (c + 1) * tc);
+  for (int t = c * tc; t < t1; ++t) {
+    if (lane < K) {
+      const int64_t a = (int64_t)t * K + lane;
+      const int e = idx[a];
+      const int slot = cnt[e];
+      cnt[e] = slot + 1;
+      slot_token[slot] = t;
       slot_gate[slot] = gate[a];
       tk_slot[a] = slot;
     }
