@@ -42,6 +42,30 @@ def expert_weight_bytes_per_matrix(cfg):
     return el * (4 if cfg.expert == "f32" else 2)
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the grouped expert GEMM from the committed counter
+    summary (FETCH_SIZE, WRITE_SIZE scaled by a plain-copy calibration), or None
+    when the kernel sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_fwd_amd", "csrc", "*"))):
+        with open(src, "rb") as f:
+            h.update(f.read())
+    w = rec.get("workloads", {}).get(workload)
+    if h.hexdigest() != rec.get("source_sha256") or not w:
+        return None
+    if w.get("fetch_kib_per_dispatch") is None or w.get("write_kib_per_dispatch") is None:
+        return None
+    return (w["fetch_kib_per_dispatch"] * rec["fetch_scale"] +
+            w["write_kib_per_dispatch"] * rec["write_scale"]) * 1024.0
+
+
 def cpu_baseline(cfg, seed, sample):
     """Time the fp64 oracle on the first `sample` tokens of the same workload."""
     import numpy as np  # noqa: F401
@@ -72,6 +96,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -82,6 +108,20 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        # A plain copy of known size: under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+        # it gives the factor between the counters and real HBM bytes.
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": max(1, args.steps)}))
+        return
 
     from sparse_moe_layer_fwd_amd import binding as B
     from sparse_moe_layer_fwd_amd.layer import DeviceLayer, x_to_device
@@ -142,6 +182,7 @@ def main():
         ach = flops_launch / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
                 "frac": round(ach / peak_f, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(cfg.name)
     roof.update({"kernel": "grouped expert GEMM (%s)" % ("skinny_kernel" if cfg.T <= 64 and cfg.act != "f32"
                                                          else "gemm_bf16_kernel" if cfg.act != "f32"
                                                          else "gemm_f32_kernel"),

@@ -74,6 +74,7 @@ struct SkinnyArgs {
   const float* b_gscale;
   int32_t N, K;
   const int* counts; const int* offs;
+  int32_t max_rows;                                   // experts with >= max_rows rows are skipped
   uint16_t* C; int64_t ldc;
   const float* row_scale;
 };
@@ -87,9 +88,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, in
 hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int* chunk_base,
-                       int* counts, int* offs, int4* tiles, int4* tiles2, int* n_tiles,
-                       hipStream_t s);
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
+                       int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
+                       int* n_tiles, hipStream_t s);
 hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
                           const int* chunk_base, const int* offs, int* slot_token,
                           float* slot_gate, int* tk_slot, hipStream_t s);

@@ -415,7 +415,7 @@ template <int BM, int BN, int BMS, int WGM, int WGN>
 hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int num_cu, hipStream_t s) {
   constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
   if (fp4) {
-    if constexpr (BMS != 0) {   // NVFP4 is used for the grouped expert GEMMs only
+    if (a.tiles) {              // NVFP4 is used for the grouped expert GEMMs only
       switch (epi) {
         case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_SQRELU_BF16>(a, grid, num_cu, s);
         case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_GATE_BF16>(a, grid, num_cu, s);
@@ -455,7 +455,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, in
     if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
     return hipErrorInvalidValue;
   }
-  if (bm == 256 && bn == 256 && bms == 64) return launch_shape<256, 256, 64, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
+  if (bm == 256 && bn == 256 && bms == 0) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
+  if (bm == 256 && bn == 256 && bms == 128) return launch_shape<256, 256, 128, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
   if (bm == 256 && bn == 128 && bms == 64) return launch_shape<256, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
   if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
   return hipErrorInvalidValue;

@@ -1,9 +1,10 @@
-// Skinny grouped expert GEMM for small batches (decode: every expert sees at
-// most T <= 64 rows).  In this regime the layer is bound by streaming expert
-// weights from HBM (the pages: latency-bound serving of tens to hundreds of
-// tokens is dominated by expert weight traffic; Korean Nemotron 3 summary,
-// section 2.2 LatentMoE), so the kernel is built to keep many bytes of each
-// expert's weights in flight and touches every weight byte exactly once.
+// Skinny grouped expert GEMM: experts with few rows.  That is every expert in
+// batch decode (T <= 64) and the cold experts of a skewed prefill batch.  Here
+// the work is bound by streaming the expert's weights from HBM (the pages:
+// latency-bound serving of tens to hundreds of tokens is dominated by expert
+// weight traffic; Korean Nemotron 3 summary, section 2.2 LatentMoE), so the
+// kernel keeps many bytes of each expert's weights in flight and reads every
+// weight byte once per 64 rows.
 //
 // Grid: (column tiles of 64, experts).  A block owns 64 output columns of one
 // expert; its 4 wavefronts split the reduction dimension in four and reduce
@@ -24,21 +25,16 @@ __device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
 }
 }  // namespace
 
+// Rows [row0, row0 + cnt) (cnt <= 64) of expert e, columns [n0, n0 + 64).
 template <bool FP4, int EPI>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
-  constexpr int MAXRB = 4;                               // up to 64 rows per expert
-  __shared__ float red[3][MAXRB * 4][4][64];             // partial sums of waves 1..3
-  const int e = blockIdx.y;
-  const int cnt = p.counts[e];
-  if (cnt == 0) return;
-  const int row0 = p.offs[e];
+__device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[16][4][64], int e,
+                                             int row0, int cnt, int n0) {
+  constexpr int MAXRB = 4;
   const int nrb = (cnt + 15) >> 4;
-  const int n0 = blockIdx.x * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = p.K >> 2;
   const int kw0 = wave * kq;
   const int grp = lane >> 4;                             // which 16-wide k slice of a 64-step
-
   const uint16_t* arow[MAXRB];
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
@@ -110,6 +106,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
     }
   }
 
+  __syncthreads();                                      // red[] free (previous chunk done)
   if (wave > 0) {
 #pragma unroll
     for (int rb = 0; rb < MAXRB; ++rb)
@@ -120,7 +117,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
           for (int i = 0; i < 4; ++i) red[wave - 1][rb * 4 + cb][i][lane] = acc[rb][cb][i];
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0) return;                                // the caller re-syncs every wavefront
   const float gs = (FP4 && p.b_gscale) ? p.b_gscale[e] : 1.0f;
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
@@ -148,6 +145,22 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
         }
       }
     }
+  }
+}
+
+// Grid (column tiles of 64, experts).  An expert with 0 < count < max_rows is
+// processed in chunks of up to 64 rows; larger experts are left to the tiled
+// GEMM.
+template <bool FP4, int EPI>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
+  __shared__ float red[3][16][4][64];                    // partial sums of waves 1..3
+  const int e = blockIdx.y;
+  const int cnt = p.counts[e];
+  if (cnt == 0 || cnt >= p.max_rows) return;
+  const int row0 = p.offs[e];
+  for (int c0 = 0; c0 < cnt; c0 += 64) {
+    skinny_chunk<FP4, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64);
+    __syncthreads();
   }
 }
 

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -33,6 +34,7 @@ namespace {
 constexpr int kTokensPerChunk = 32;   // routing chunk: one histogram row / one scatter wavefront
 constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
 constexpr int kSmallBM = 64;          // grouped bf16 GEMM: height of each expert's remainder tiles
+constexpr int kSmallBM256 = 128;      // ... when the full tiles are 256 rows high
 constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -91,6 +93,7 @@ struct Plan {
   size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
   size_t slot_token, slot_gate, tk_slot, H, O, u, Hs, ys, total;
   int nchunks, bm, bms, max_tiles, max_tiles2;
+  int cold;        // prefill: experts with fewer rows go to the skinny kernel (0: none)
   bool f32, skinny;
 };
 
@@ -114,10 +117,19 @@ Plan make_plan(const moe_config_t& c, int T) {
     p.bms = 0;
     p.max_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
     p.max_tiles2 = 0;
+  } else if (Tz * K >= 256 * N) {
+    // large prefill: full 256-row tiles, each expert's remaining rows in
+    // 128-row tiles.  (Sending the cold experts to the skinny kernel instead,
+    // with a 64- or 256-row cutoff, measured no faster on MI355X.)
+    p.bm = 256;
+    p.bms = kSmallBM256;
+    p.cold = 0;
+    p.max_tiles = (int)((Tz * K) / p.bm);
+    p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
   } else {
-    // full tiles of 256 rows when experts average >= 256 rows, else 128; the
-    // rows left over in each expert go to 64-row tiles
-    p.bm = (Tz * K >= 256 * N) ? 256 : 128;
+    // smaller batches: full 128-row tiles plus 64-row tiles for each
+    // expert's remainder
+    p.bm = 128;
     p.bms = kSmallBM;
     p.max_tiles = (int)((Tz * K) / p.bm);
     p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
@@ -225,7 +237,7 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
                         at<int>(ws, p.idx), at<float>(ws, p.gate), at<int>(ws, p.ccount), s));
   }
   StageScope sc(MOE_STAGE_SCAN, s);
-  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, p.bms,
+  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, p.bms, p.cold,
                       at<int>(ws, p.cbase), at<int>(ws, p.counts), at<int>(ws, p.offs),
                       at<int4>(ws, p.tiles), at<int4>(ws, p.tiles2), at<int>(ws, p.ntiles), s));
   return MOE_OK;
@@ -255,20 +267,22 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   const float* G = up ? w.w1_gscale : w.w2_gscale;
   const int cap = h->num_cu * 2;
   StageScope sc(up ? MOE_STAGE_EXPERT_UP : MOE_STAGE_EXPERT_DOWN, s);
+  SkinnyArgs sk;
+  memset(&sk, 0, sizeof(sk));
+  sk.A = (const uint16_t*)A; sk.lda = kdim; sk.a_rows = a_rows;
+  sk.B = B;
+  sk.ldb = fp4 ? kdim / 2 : kdim;
+  sk.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
+  sk.b_scale = S; sk.lds_scale = kdim / 16; sk.s_gstride = rows * kdim / 16;
+  sk.b_gscale = G;
+  sk.N = (int)rows; sk.K = (int)kdim;
+  sk.counts = at<int>(ws, p.counts); sk.offs = at<int>(ws, p.offs);
+  sk.max_rows = p.skinny ? INT32_MAX : p.cold;
+  sk.C = (uint16_t*)C; sk.ldc = rows;
+  sk.row_scale = at<float>(ws, p.slot_gate);
+  const int epi = up ? EPI_SQRELU_BF16 : EPI_GATE_BF16;
   if (p.skinny) {
-    SkinnyArgs a;
-    memset(&a, 0, sizeof(a));
-    a.A = (const uint16_t*)A; a.lda = kdim; a.a_rows = a_rows;
-    a.B = B;
-    a.ldb = fp4 ? kdim / 2 : kdim;
-    a.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
-    a.b_scale = S; a.lds_scale = kdim / 16; a.s_gstride = rows * kdim / 16;
-    a.b_gscale = G;
-    a.N = (int)rows; a.K = (int)kdim;
-    a.counts = at<int>(ws, p.counts); a.offs = at<int>(ws, p.offs);
-    a.C = (uint16_t*)C; a.ldc = rows;
-    a.row_scale = at<float>(ws, p.slot_gate);
-    MOE_TRY(launch_skinny(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, c.n_experts, s));
+    MOE_TRY(launch_skinny(sk, fp4, epi, c.n_experts, s));
     return MOE_OK;
   }
   GemmArgs a = gemm_args();
@@ -286,13 +300,13 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   if (p.f32) {
     a.M = p.max_tiles;   // grouped: upper bound on row tiles (grid sizing)
     MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_GATE_F32, cap, s));
-  } else {
-    const int bn = p.bm == 256 ? 256 : 128;
-    const int64_t ntn = (rows + bn - 1) / bn;
-    const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
-    MOE_TRY(launch_gemm_bf16(a, fp4, up ? EPI_SQRELU_BF16 : EPI_GATE_BF16, p.bm, bn, p.bms,
-                             items, h->num_cu, s));
+    return MOE_OK;
   }
+  const int bn = p.bm == 256 ? 256 : 128;
+  const int64_t ntn = (rows + bn - 1) / bn;
+  const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
+  MOE_TRY(launch_gemm_bf16(a, fp4, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+  if (p.cold > 0) MOE_TRY(launch_skinny(sk, fp4, epi, c.n_experts, s));
   return MOE_OK;
 }
 

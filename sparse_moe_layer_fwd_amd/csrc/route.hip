@@ -141,12 +141,14 @@ __device__ int block_excl_scan_1024(int v, int* total_out) {
 }
 
 // Single block: per-expert totals over chunks (chunk_base = exclusive prefix
-// over chunks), expert offsets, and the grouped-GEMM row-tile lists.  With
-// bms == 0 every expert's rows are cut into tiles of height bm (list 0).  With
-// bms > 0 list 0 holds only full tiles of height bm and list 1 covers each
-// expert's remaining rows with tiles of height bms.  n_tiles[0..1] = list sizes.
+// over chunks), expert offsets, and the grouped-GEMM row-tile lists.  Experts
+// with fewer than min_rows rows get no tiles (the skinny kernel takes them).
+// With bms == 0 every other expert's rows are cut into tiles of height bm
+// (list 0).  With bms > 0 list 0 holds only full tiles of height bm and list 1
+// covers each expert's remaining rows with tiles of height bms.
+// n_tiles[0..1] = list sizes.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_counts,
-                                                    int nchunks, int N, int bm, int bms,
+                                                    int nchunks, int N, int bm, int bms, int min_rows,
                                                     int* __restrict__ chunk_base,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offs,
@@ -175,8 +177,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   }
   int all = 0;
   const int off = block_excl_scan_1024(total, &all);
-  const int nbig = bms > 0 ? total / bm : (total + bm - 1) / bm;
-  const int rem = bms > 0 ? total - nbig * bm : 0;
+  const bool tiled = total >= min_rows;
+  const int nbig = !tiled ? 0 : bms > 0 ? total / bm : (total + bm - 1) / bm;
+  const int rem = bms > 0 && tiled ? total - nbig * bm : 0;
   const int nsmall = bms > 0 ? (rem + bms - 1) / bms : 0;
   int all_big = 0, all_small = 0;
   const int toff = block_excl_scan_1024(nbig, &all_big);
@@ -197,11 +200,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   }
 }
 
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int* chunk_base,
-                       int* counts, int* offs, int4* tiles, int4* tiles2, int* n_tiles,
-                       hipStream_t s) {
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
+                       int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
+                       int* n_tiles, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm, bms,
-                     chunk_base, counts, offs, tiles, tiles2, n_tiles);
+                     min_rows, chunk_base, counts, offs, tiles, tiles2, n_tiles);
   return hipGetLastError();
 }
 

@@ -104,6 +104,14 @@ SMALL = {
     "k_equals_n": MoEConfig("k_equals_n", T=90, d=256, latent=128, n_experts=6, top_k=6, ffn=128),
     "many_experts_small_batch": MoEConfig("many_experts_small_batch", T=70, d=256, latent=128,
                                           n_experts=1000, top_k=12, ffn=128),
+    # T*K >= 256*N: hot experts on 256-row tiles, cold experts on the skinny kernel
+    "hot_cold_bf16": MoEConfig("hot_cold_bf16", T=600, d=512, latent=256, n_experts=8, top_k=4,
+                               ffn=256, zipf_s=1.1),
+    "hot_cold_nvfp4": MoEConfig("hot_cold_nvfp4", T=700, d=512, latent=256, n_experts=8, top_k=4,
+                                ffn=512, expert="nvfp4", zipf_s=1.1),
+    # same regime with l not a multiple of 256: every expert on 256-row tiles
+    "big_tiles_no_cold": MoEConfig("big_tiles_no_cold", T=600, d=256, latent=192, n_experts=8,
+                                   top_k=4, ffn=128, zipf_s=1.1),
 }
 
 
@@ -174,7 +182,7 @@ class _DecodedBf16(Workload):
         return f32_to_bf16_bits(oracle.decode_expert(self._fp4.w2(e), "nvfp4").astype(np.float32))
 
 
-@pytest.mark.parametrize("name", ["latent_nvfp4_prefill_zipf", "decode_nvfp4"])
+@pytest.mark.parametrize("name", ["latent_nvfp4_prefill_zipf", "decode_nvfp4", "hot_cold_nvfp4"])
 def test_nvfp4_path_bitwise_equals_bf16_path_on_decoded_weights(name):
     """In-register NVFP4 decode is exact: with a unit global scale the NVFP4 path
     and the bf16 path on the decoded weights give bitwise the same y."""
