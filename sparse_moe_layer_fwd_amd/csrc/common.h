@@ -39,16 +39,17 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 
 // ------------------------------------------------------------------ kernel params
 enum Epi : int {
-  EPI_BF16 = 0,        // C(bf16) = acc
+  EPI_BF16 = 0,        // C(bf16) = g*acc                             (expert down, dense)
   EPI_Z = 1,           // C(f32) = acc and C2(bf16) = acc             (latent z32 / z16)
   EPI_SQRELU_BF16 = 2, // C(bf16) = max(g*acc,0)^2                    (expert up)
-  EPI_GATE_BF16 = 3,   // C(bf16) = row_scale[r]*g*acc                (expert down)
   EPI_F32 = 4,         // C(f32) = acc (+ bias[col])                  (router, shared down)
   EPI_BF16_ADD = 5,    // C(bf16) = acc + add[r][c] (fp32)            (up-proj + shared)
   EPI_SQRELU_F32 = 6,  // C(f32) = max(acc,0)^2
-  EPI_GATE_F32 = 7,    // C(f32) = row_scale[r]*acc
   EPI_F32_ADD = 8      // C(f32) = acc + add[r][c]
 };
+// g: the NVFP4 per-expert global scale (1 for bf16 weights).  Gates are not
+// applied by any GEMM: the combine step multiplies each expert output by its
+// gate while summing a token's K outputs.
 
 // A tile row source.  Logical row r of the GEMM reads physical row
 // a_rows ? a_rows[r] : r of A.
@@ -62,7 +63,6 @@ struct GemmArgs {
   const int4* tiles; const int* n_tiles;              // grouped: (group, row0, row1, -)
   const int4* tiles2;                                 // grouped: second (remainder) list
   void* C; int64_t ldc; void* C2; int64_t ldc2;
-  const float* row_scale;                             // per logical row (gates)
   const float* bias;                                  // per column
   const float* add; int64_t ld_add;                   // fp32 addend
 };
@@ -76,7 +76,6 @@ struct SkinnyArgs {
   const int* counts; const int* offs;
   int32_t max_rows;                                   // experts with >= max_rows rows are skipped
   uint16_t* C; int64_t ldc;
-  const float* row_scale;
 };
 
 // ------------------------------------------------------------------ launchers
@@ -91,10 +90,10 @@ hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* id
 hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
                        int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
                        int* n_tiles, hipStream_t s);
-hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
-                          const int* chunk_base, const int* offs, int* slot_token,
-                          float* slot_gate, int* tk_slot, hipStream_t s);
-hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot, int T, int K,
-                          int W, const float* add, void* out, bool out_f32, hipStream_t s);
+hipError_t launch_scatter(const int* idx, int T, int K, int N, int tc, const int* chunk_base,
+                          const int* offs, int* slot_token, int* tk_slot, hipStream_t s);
+hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot,
+                          const float* gate, int T, int K, int W, const float* add, void* out,
+                          bool out_f32, hipStream_t s);
 
 }  // namespace moe

@@ -15,7 +15,8 @@
 // Data movement: operands go global -> LDS with gfx950's direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
 // through a ring of NST stages, so NST-1 k-tiles are in flight while one is
-// multiplied and no VGPRs are spent on staging.  Each wavefront waits for its
+// multiplied and no VGPRs are spent on staging.  The ring runs continuously
+// over each persistent block's sequence of output tiles.  Each wavefront waits for its
 // own loads with an explicit vmcnt, then a bare s_barrier publishes the stage.
 // LDS rows hold BK bf16 as 16-byte chunks; chunk c of row r sits at c ^ f(r),
 // which spreads the fragment reads of 8 or 16 consecutive rows over distinct
@@ -104,53 +105,149 @@ struct TileCfg {
   static constexpr int B_BYTES = FP4 ? BQ_BYTES + BS_BYTES : BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int BDQ = FP4 ? BN * BK * 2 : 0;            // decoded B (double-buffered)
-  static constexpr int LDS = NST * STAGE + 2 * BDQ;
+  // bf16 weights: epilogue staging, one 32-row block per wavefront row (NVFP4
+  // tiles spend that LDS on a deeper ring and store directly)
+  static constexpr int EPB = FP4 ? 0 : 32 * WGM * BN * 2;
+  static constexpr int LDS = NST * STAGE + 2 * BDQ + EPB;
   static constexpr int A_TOT = BM * CPR / 64;                  // 1 KB DMA blocks per k-tile
   static constexpr int B_TOT = FP4 ? BQ_BYTES / 1024 : BN * CPR / 64;
   static constexpr int S_TOT = FP4 ? BS_BYTES / 256 : 0;       // dword-per-lane DMA blocks
   static constexpr int A_PW = (A_TOT + NW - 1) / NW;           // per wavefront
   static constexpr int B_PW = (B_TOT + NW - 1) / NW;
   static constexpr int S_PW = (S_TOT + NW - 1) / NW;
+  static constexpr int S_PW1 = S_PW > 0 ? S_PW : 1;
+  static constexpr int S_TOT1 = S_TOT > 0 ? S_TOT : 1;
   static constexpr int LOADS = A_PW + B_PW + S_PW;             // vm ops per wave per k-tile
+  static constexpr int WM = BM / WGM, WN = BN / WGN;           // wavefront tile
+  static constexpr int TM = WM / 32, TN = WN / 32;             // 32x32 MFMA blocks per wavefront
   static_assert(A_TOT >= 1 && B_TOT >= 1 && (!FP4 || S_TOT >= 1), "tile too small");
-  static_assert(LOADS * (NST - 2) < 64, "vmcnt range");
+  static_assert(LOADS * (NST - 1) < 64, "vmcnt range");
+  // staged bf16 epilogue: 16-byte stores per thread and tile (all issued)
+  static constexpr int EPI_STORES = TM * (32 * WGM * (BN / 8)) / NT;
   static_assert(STAGE % 16 == 0, "stage alignment");
+  static_assert(TM >= 1 && TN >= 1, "wave tile");
+  // NVFP4 decodes k-tile t + 1 while the ring refills the stage of t - 1
+  static_assert(!FP4 || NST >= 3, "NVFP4 ring");
 };
 
-// One output tile: rows [r0, r1) (r1 - r0 <= BM) of group g, columns [n0, n0 + BN).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, int r0, int r1,
-                                          int n0) {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Load through the scalar unit; the address must be wavefront-uniform.  Scalar
+// loads count on lgkmcnt, so waiting for them never drains the direct-to-LDS
+// loads in flight (vmcnt), as a vector load of the tile list, the row indices
+// or the global scale would.
+template <class T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// Wait until at most `pd` k-tiles of LOADS vector-memory ops each (the newest
+// ones) plus EXTRA further ops issued after them (an epilogue's stores) are
+// still in flight; pd is wavefront-uniform and <= MAXPD.  Any other ops issued
+// after those loads also count, which only makes it wait longer.
+template <int LOADS, int MAXPD, int EXTRA = 0>
+__device__ __forceinline__ void wait_tiles(int pd) {
+  static_assert(MAXPD * LOADS + EXTRA < 64, "vmcnt range");
+  if constexpr (MAXPD >= 5) {
+    if (pd >= 5) { wait_vm<5 * LOADS + EXTRA>(); return; }
+  }
+  if constexpr (MAXPD >= 4) {
+    if (pd >= 4) { wait_vm<4 * LOADS + EXTRA>(); return; }
+  }
+  if constexpr (MAXPD >= 3) {
+    if (pd >= 3) { wait_vm<3 * LOADS + EXTRA>(); return; }
+  }
+  if constexpr (MAXPD >= 2) {
+    if (pd >= 2) { wait_vm<2 * LOADS + EXTRA>(); return; }
+  }
+  if constexpr (MAXPD >= 1) {
+    if (pd >= 1) { wait_vm<LOADS + EXTRA>(); return; }
+  }
+  wait_vm<EXTRA>();
+}
+
+// Wait for k-tile `need` of a stream that has issued `issued` k-tiles, the
+// last epilogue's STORES stores going out after k-tile `st_tile`.
+template <int LOADS, int MAXPD, int STORES>
+__device__ __forceinline__ void wait_tile(int need, int issued, int st_tile) {
+  if (STORES > 0 && need <= st_tile) wait_tiles<LOADS, MAXPD, STORES>(issued - 1 - need);
+  else wait_tiles<LOADS, MAXPD, 0>(issued - 1 - need);
+}
+
+// Global sources of one output tile: rows [r0, r1) of group g, columns
+// [n0, n0 + BN), as tile-uniform bases plus this lane's 32-bit offsets.
+template <class C>
+struct TileSrc {
+  int g, r0, r1, n0;
+  const uint16_t* A;
+  const char* B;
+  const char* S;
+  uint32_t aoff[C::A_PW], boff[C::B_PW], soff[C::S_PW1];
+};
+
+// Row tile `rt`, column tile `nt` of a list (or of the dense row blocks).
+template <int BM, int BN>
+__device__ __forceinline__ void item_coords(const GemmArgs& p, const int4* list, int nrt, int ntn,
+                                            int it, int& g, int& r0, int& r1, int& n0) {
+  int rt = it / ntn, nt = it - rt * ntn;
+  if (!list && ntn > 8) {
+    // dense and wide: walk bands of 4 row tiles column by column, so the 32
+    // consecutive items of one XCD reuse 4 A and 8 B strips from its L2
+    const int band = it / (4 * ntn), in = it - band * 4 * ntn;
+    const int rows = min(4, nrt - band * 4);
+    rt = band * 4 + in % rows;
+    nt = in / rows;
+  }
+  if (list) {
+    g = sload(&list[rt].x); r0 = sload(&list[rt].y); r1 = sload(&list[rt].z);
+  } else {
+    g = 0; r0 = rt * BM; r1 = min(p.M, r0 + BM);
+  }
+  n0 = nt * BN;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+__device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r1, int n0,
+                                         TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& s) {
   using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
   constexpr int CPR = C::CPR, NW = C::NW;
-  constexpr int WM = BM / WGM, WN = BN / WGN;      // wavefront tile
-  constexpr int TM = WM / 32, TN = WN / 32;        // 32x32 MFMA blocks per wavefront
-  constexpr int S_PW1 = C::S_PW > 0 ? C::S_PW : 1;
-  constexpr int S_TOT1 = C::S_TOT > 0 ? C::S_TOT : 1;
-  static_assert(TM >= 1 && TN >= 1, "wave tile");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int nk = p.K / BK;
-
-  // the previous tile's stores must not be counted as in-flight loads below
-  wait_vm<0>();
-
-  // ---- per-lane global offsets of this lane's chunks (32-bit, from uniform bases)
-  const uint16_t* Abase = (const uint16_t*)p.A;
-  uint32_t aoff[C::A_PW];
+  constexpr int RPB = 64 / CPR;                    // A rows per 1 KB DMA block
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  s.g = g; s.r0 = r0; s.r1 = r1; s.n0 = n0;
+  s.A = (const uint16_t*)p.A;
 #pragma unroll
   for (int j = 0; j < C::A_PW; ++j) {
     const int blk = (wave + j * NW) % C::A_TOT;
     const int q = blk * 64 + lane;                 // LDS chunk index in the A region
-    const int row = q / CPR, pos = q % CPR;
-    const int lr = min(r0 + row, r1 - 1);          // rows past the end re-read the last row
-    const uint32_t pr = p.a_rows ? (uint32_t)p.a_rows[lr] : (uint32_t)lr;
-    aoff[j] = pr * (uint32_t)p.lda + swz_chunk<CPR>(row, pos) * 8;
+    const int row = q / CPR, pos = q % CPR;        // row = blk * RPB + lane / CPR
+    uint32_t pr;
+    if (p.a_rows) {
+      // the block's RPB row indices through the scalar unit (the index array
+      // is padded, so reading up to RPB - 1 entries past r1 stays in bounds),
+      // then each lane picks its own; rows past the end re-read the last row
+      const int rb = r0 + blk * RPB;
+      const int last = sload(p.a_rows + (r1 - 1));
+      int pick = last;
+      if (rb < r1) {
+        int v[RPB];
+#pragma unroll
+        for (int u = 0; u < RPB; ++u) v[u] = sload(p.a_rows + rb + u);
+        const int sub = lane / CPR;
+        pick = v[0];
+#pragma unroll
+        for (int u = 1; u < RPB; ++u) pick = sub == u ? v[u] : pick;
+        if (rb + sub >= r1) pick = last;
+      }
+      pr = (uint32_t)pick;
+    } else {
+      pr = (uint32_t)min(r0 + row, r1 - 1);        // rows past the end re-read the last row
+    }
+    s.aoff[j] = pr * (uint32_t)p.lda + swz_chunk<CPR>(row, pos) * 8;
   }
-  const char* Bbase = FP4 ? (const char*)p.B + (int64_t)g * p.b_gstride
-                          : (const char*)((const uint16_t*)p.B + (int64_t)g * p.b_gstride);
-  const char* Sbase = FP4 ? (const char*)p.b_scale + (int64_t)g * p.s_gstride : nullptr;
-  uint32_t boff[C::B_PW], soff[S_PW1];
+  s.B = FP4 ? (const char*)p.B + (int64_t)g * p.b_gstride
+            : (const char*)((const uint16_t*)p.B + (int64_t)g * p.b_gstride);
+  s.S = FP4 ? (const char*)p.b_scale + (int64_t)g * p.s_gstride : nullptr;
 #pragma unroll
   for (int j = 0; j < C::B_PW; ++j) {
     const int blk = (wave + j * NW) % C::B_TOT;
@@ -158,52 +255,239 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
       constexpr int QPR = BK / 32;
       const int q = blk * 64 + lane, row = q / QPR, pos = q % QPR;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
-      boff[j] = n * (uint32_t)p.ldb + pos * 16;    // bytes
+      s.boff[j] = n * (uint32_t)p.ldb + pos * 16;  // bytes
     } else {
       const int q = blk * 64 + lane, row = q / CPR, pos = q % CPR;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
-      boff[j] = n * (uint32_t)p.ldb + swz_chunk<CPR>(row, pos) * 8;   // elements
+      s.boff[j] = n * (uint32_t)p.ldb + swz_chunk<CPR>(row, pos) * 8;   // elements
     }
   }
 #pragma unroll
-  for (int j = 0; j < S_PW1; ++j) {
-    const int blk = (wave + j * NW) % S_TOT1;
+  for (int j = 0; j < C::S_PW1; ++j) {
+    const int blk = (wave + j * NW) % C::S_TOT1;
     const uint32_t n = (uint32_t)min(n0 + blk * 64 + lane, p.N - 1);
-    soff[j] = n * (uint32_t)p.lds_scale;           // bytes; the k-tile's BK/16 scale bytes sit in
-                                                   // the aligned dword loaded per row
+    s.soff[j] = n * (uint32_t)p.lds_scale;         // bytes; the k-tile's BK/16 scale bytes sit
+                                                   // in the aligned dword loaded per row
   }
+}
 
-  // ---- issue the direct-to-LDS loads of k-tile kt into stage st
-#define MOE_ISSUE(KT, ST)                                                                     \
-  do {                                                                                        \
-    char* S_ = smem + (ST) * C::STAGE;                                                        \
-    const uint32_t k0_ = (uint32_t)(KT) * BK;                                                 \
-    _Pragma("unroll") for (int j = 0; j < C::A_PW; ++j) {                                     \
-      const int blk = (wave + j * NW) % C::A_TOT;                                             \
-      dma16(Abase + (aoff[j] + k0_), S_ + blk * 1024);                                        \
-    }                                                                                         \
-    if (FP4) {                                                                                \
-      _Pragma("unroll") for (int j = 0; j < C::B_PW; ++j) {                                   \
-        const int blk = (wave + j * NW) % C::B_TOT;                                           \
-        dma16(Bbase + (boff[j] + k0_ / 2), S_ + C::A_BYTES + blk * 1024);                     \
-      }                                                                                       \
-      _Pragma("unroll") for (int j = 0; j < C::S_PW; ++j) {                                   \
-        const int blk = (wave + j * NW) % S_TOT1;                                             \
-        dma_small<4>(Sbase + ((soff[j] + k0_ / 16) & ~3u), S_ + C::A_BYTES + C::BQ_BYTES + blk * 256); \
-      }                                                                                       \
-    } else {                                                                                  \
-      const uint16_t* Bk_ = (const uint16_t*)Bbase + k0_;                                     \
-      if (p.kseg < p.K) {             /* B stored as k segments (shared experts' W2) */       \
-        const int seg_ = (int)(k0_ / (uint32_t)p.kseg);                                       \
-        Bk_ = (const uint16_t*)Bbase + (int64_t)seg_ * p.b_segstride +                        \
-              (k0_ - (uint32_t)seg_ * p.kseg);                                                \
-      }                                                                                       \
-      _Pragma("unroll") for (int j = 0; j < C::B_PW; ++j) {                                   \
-        const int blk = (wave + j * NW) % C::B_TOT;                                           \
-        dma16(Bk_ + boff[j], S_ + C::A_BYTES + blk * 1024);                                   \
-      }                                                                                       \
-    }                                                                                         \
-  } while (0)
+// Direct-to-LDS loads of k-tile kt of a tile into one stage.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+__device__ __forceinline__ void issue_tile(const GemmArgs& p,
+                                           const TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& s,
+                                           int kt, char* stage) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  constexpr int NW = C::NW;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t k0 = (uint32_t)kt * BK;
+#pragma unroll
+  for (int j = 0; j < C::A_PW; ++j) {
+    const int blk = (wave + j * NW) % C::A_TOT;
+    dma16(s.A + (s.aoff[j] + k0), stage + blk * 1024);
+  }
+  if (FP4) {
+#pragma unroll
+    for (int j = 0; j < C::B_PW; ++j) {
+      const int blk = (wave + j * NW) % C::B_TOT;
+      dma16(s.B + (s.boff[j] + k0 / 2), stage + C::A_BYTES + blk * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < C::S_PW; ++j) {
+      const int blk = (wave + j * NW) % C::S_TOT1;
+      dma_small<4>(s.S + ((s.soff[j] + k0 / 16) & ~3u), stage + C::A_BYTES + C::BQ_BYTES + blk * 256);
+    }
+  } else {
+    const uint16_t* Bk = (const uint16_t*)s.B + k0;
+    if (p.kseg < p.K) {                    // B stored as k segments (shared experts' W2)
+      const int seg = (int)(k0 / (uint32_t)p.kseg);
+      Bk = (const uint16_t*)s.B + (int64_t)seg * p.b_segstride + (k0 - (uint32_t)seg * p.kseg);
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_PW; ++j) {
+      const int blk = (wave + j * NW) % C::B_TOT;
+      dma16(Bk + s.boff[j], stage + C::A_BYTES + blk * 1024);
+    }
+  }
+}
+
+// NVFP4: decode the raw codes of k-tile kt (its position inside its tile's K
+// loop) from `stage` into the bf16 buffer D.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+__device__ __forceinline__ void decode_tile(const char* stage, uint4* D, int kt) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  constexpr int CPR = C::CPR;
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
+  const uint8_t* Sc = Q + C::BQ_BYTES;
+  constexpr int UNITS = BN * BK / 16;              // one 16-code block per unit
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
+    const int u = u0 + tid;
+    if (UNITS % C::NT == 0 || u < UNITS) {
+      const int row = u / (BK / 16), blk = u % (BK / 16);
+      const uint2 q = *reinterpret_cast<const uint2*>(Q + row * (BK / 2) + blk * 8);
+      const Fp4Scale sc = split_scale(Sc[row * 4 + ((kt * (BK / 16)) & 3) + blk]);
+      D[row * CPR + swz_chunk<CPR>(row, 2 * blk + 0)] = fp4x8(q.x, sc);
+      D[row * CPR + swz_chunk<CPR>(row, 2 * blk + 1)] = fp4x8(q.y, sc);
+    }
+  }
+}
+
+// acc += A_stage * B_stage^T for one k-tile (the MFMA computes C^T: weights as
+// its A operand, activations as its B operand).
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+__device__ __forceinline__ void mma_tile(
+    const uint4* As, const uint4* Bs,
+    f32x16 (&acc)[TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TN][TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TM]) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  constexpr int CPR = C::CPR, TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    const int ch = s * 2 + (lane >> 5);
+    bf16x8 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = wn * WN + j * 32 + (lane & 31);
+      b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
+  }
+}
+
+// Epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
+// col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
+// bf16 outputs go through LDS (`stage`, EPB bytes): a lane's own values cover
+// 16 bytes of each of 32 rows per store, so they are transposed one i-block
+// (32 rows per wavefront row) at a time and written back as whole 16-byte
+// units, each wavefront store covering complete rows of the tile.  Contains
+// barriers: every wavefront of the block calls it.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+__device__ __forceinline__ void epilogue_tile(
+    const GemmArgs& p, int g, int r0, int r1, int n0, char* stage,
+    f32x16 (&acc)[TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TN][TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TM]) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const float gs = (FP4 && p.b_gscale) ? sload(p.b_gscale + g) : 1.0f;
+  if constexpr ((EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) && !FP4) {
+    constexpr int U = BN / 8;                      // 16-byte units per staged row
+    constexpr int ROWS = 32 * WGM;                 // staged rows per i-block
+    constexpr int PER = ROWS * U / C::NT;          // units stored per thread
+    static_assert(ROWS * U % C::NT == 0, "epilogue units");
+    const int lr = wm * 32 + (lane & 31);          // this lane's staged row
+    // stores through a buffer resource over the tile's rows: lanes past the
+    // tile's last row or column get an out-of-range offset and are dropped by
+    // the hardware, so every thread issues all EPI_STORES stores (the k-loop
+    // waits count them)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (uint16_t*)p.C + (int64_t)r0 * p.ldc, 0, (r1 - r0) * (int)p.ldc * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v0 = acc[j][i][4 * q + 0], v1 = acc[j][i][4 * q + 1];
+          float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
+          if (EPI == EPI_SQRELU_BF16) {
+            v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
+            v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
+            v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
+          } else if (FP4) {
+            v0 *= gs; v1 *= gs; v2 *= gs; v3 *= gs;
+          }
+          const int lc = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          const int u = (lc >> 3) ^ (lr & (U - 1));
+          *reinterpret_cast<uint2*>(stage + lr * (BN * 2) + u * 16 + (lc & 7) * 2) =
+              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+        }
+      }
+      bar_lds();                                   // i-block staged by every wavefront
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int gidx = threadIdx.x + k * C::NT;
+        const int row = gidx / U, un = gidx % U;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + (un ^ (row & (U - 1))) * 16);
+        const int lrow = (row >> 5) * WM + i * 32 + (row & 31);   // row within the tile
+        const int col = n0 + un * 8;
+        const int off = (r0 + lrow < r1 && col < p.N) ? (lrow * (int)p.ldc + col) * 2 : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
+      }
+      bar_lds();                                   // staging free for the next i-block
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = r0 + wm * WM + i * 32 + (lane & 31);
+      if (row >= r1) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (col >= p.N) continue;
+          float v0 = acc[j][i][4 * q + 0], v1 = acc[j][i][4 * q + 1];
+          float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
+          const int64_t o = (int64_t)row * p.ldc + col;
+          if (EPI == EPI_F32) {
+            *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
+          } else if (EPI == EPI_Z) {
+            *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
+            *reinterpret_cast<uint2*>((uint16_t*)p.C2 + (int64_t)row * p.ldc2 + col) =
+                make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+          } else {
+            if (EPI == EPI_BF16_ADD) {
+              const float4 ad = *reinterpret_cast<const float4*>(p.add + (int64_t)row * p.ld_add + col);
+              v0 += ad.x; v1 += ad.y; v2 += ad.z; v3 += ad.w;
+            } else if (EPI == EPI_SQRELU_BF16) {
+              v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
+              v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
+              v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
+            } else {                               // EPI_BF16
+              v0 *= gs; v1 *= gs; v2 *= gs; v3 *= gs;
+            }
+            *reinterpret_cast<uint2*>((uint16_t*)p.C + o) =
+                make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+          }
+        }
+      }
+    }
+  }
+}
+
+// NVFP4 weights: one output tile (rows [r0, r1) of expert g, columns [n0,
+// n0 + BN)).  The raw codes and scales of k-tile t + 1 are decoded into a
+// bf16 buffer (two of them, alternating) while k-tile t is multiplied, so each
+// wait covers the k-tile about to be decoded; the ring keeps NST - 2 further
+// k-tiles in flight.  Every tile restarts the ring (measured faster for these
+// tiles than running it across tiles).
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+__device__ __forceinline__ void fp4_tile(const GemmArgs& p, char* smem, int g, int r0, int r1, int n0) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, true>;
+  constexpr int TM = C::TM, TN = C::TN;
+  const int nk = p.K / BK;                          // >= NST - 1 (checked by the launcher)
+  uint4* D0 = reinterpret_cast<uint4*>(smem + NST * C::STAGE);
+  TileSrc<C> src;
+  make_src<BM, BN, BK, WGM, WGN, NST, true>(p, g, r0, r1, n0, src);
+  bar_lds();     // every wavefront is done with the previous tile's stages
+  wait_vm<0>();  // and its stores: only this tile's loads are counted below
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, true>(p, src, s, smem + s * C::STAGE);
+  wait_tiles<C::LOADS, NST - 2>(NST - 2);           // k-tile 0 landed
+  bar();
+  decode_tile<BM, BN, BK, WGM, WGN, NST, true>(smem, D0, 0);
 
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -213,185 +497,231 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, char* smem, int g, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
 
-  // ---- NVFP4: decode raw k-tile KT (stage KT % NST) into bf16 buffer KT & 1
-#define MOE_DECODE(KT)                                                                        \
-  do {                                                                                        \
-    const char* S_ = smem + ((KT) % NST) * C::STAGE;                                          \
-    uint4* D_ = reinterpret_cast<uint4*>(smem + NST * C::STAGE + ((KT) & 1) * C::BDQ);         \
-    const uint8_t* Q_ = reinterpret_cast<const uint8_t*>(S_ + C::A_BYTES);                    \
-    const uint8_t* Sc_ = Q_ + C::BQ_BYTES;                                                    \
-    constexpr int UNITS = BN * BK / 16;             /* one 16-code block per unit */            \
-    _Pragma("unroll") for (int u0 = 0; u0 < UNITS; u0 += C::NT) {                             \
-      const int u = u0 + tid;                                                                 \
-      if (UNITS % C::NT == 0 || u < UNITS) {                                                  \
-        const int row = u / (BK / 16), blk = u % (BK / 16);                                   \
-        const uint2 q = *reinterpret_cast<const uint2*>(Q_ + row * (BK / 2) + blk * 8);       \
-        const Fp4Scale sc = split_scale(Sc_[row * 4 + (((KT) * (BK / 16)) & 3) + blk]);       \
-        D_[row * CPR + swz_chunk<CPR>(row, 2 * blk + 0)] = fp4x8(q.x, sc);                    \
-        D_[row * CPR + swz_chunk<CPR>(row, 2 * blk + 1)] = fp4x8(q.y, sc);                    \
-      }                                                                                       \
-    }                                                                                         \
-  } while (0)
-  // wait until this wavefront's loads of some k-tile are done, given that at
-  // most `pending` later k-tiles' loads may stay in flight (in-order completion)
-#define MOE_WAIT(PENDING)                                                                     \
-  do {                                                                                        \
-    const int pd_ = (PENDING);                                                                \
-    if (NST >= 4 && pd_ >= 2) wait_vm<(NST >= 4 ? 2 : 0) * C::LOADS>();                       \
-    else if (pd_ >= 1) wait_vm<C::LOADS>();                                                   \
-    else wait_vm<0>();                                                                        \
-  } while (0)
-
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nk) MOE_ISSUE(s, s);
-  if (FP4) {                                        // decode k-tile 0 ahead of the loop
-    MOE_WAIT(min(nk - 1, NST - 2));
-    bar();
-    MOE_DECODE(0);
-  }
-
   for (int kt = 0; kt < nk; ++kt) {
-    // bf16: k-tile kt must have landed.  NVFP4: the raw codes of kt + 1 too,
-    // because they are decoded while k-tile kt is multiplied.
-    const int need = FP4 ? min(kt + 1, nk - 1) : kt;
-    MOE_WAIT(min(nk - 1 - need, NST - 2));
-    if (FP4) bar_lds(); else bar();                 // stages (and decoded B) complete for all waves
-    if (kt + NST - 1 < nk) MOE_ISSUE(kt + NST - 1, (kt + NST - 1) % NST);
-    if (FP4 && kt + 1 < nk) MOE_DECODE(kt + 1);
-    const char* S = smem + (kt % NST) * C::STAGE;
-    const uint4* As = reinterpret_cast<const uint4*>(S);
-    const uint4* Bs = FP4 ? reinterpret_cast<const uint4*>(smem + NST * C::STAGE + (kt & 1) * C::BDQ)
-                          : reinterpret_cast<const uint4*>(S + C::A_BYTES);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int ch = s * 2 + (lane >> 5);
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = wn * WN + j * 32 + (lane & 31);
-        b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
-    }
+    // the raw k-tile decoded in this iteration (kt + 1) must have landed; the
+    // k-tiles issued after it may stay in flight (in-order completion)
+    const int need = kt + 1 < nk ? kt + 1 : kt;
+    const int issued = kt + NST - 1 < nk ? kt + NST - 1 : nk;
+    wait_tiles<C::LOADS, NST - 2>(issued - 1 - need);
+    bar_lds();                                      // stages and decoded buffer kt complete
+    if (kt + NST - 1 < nk)                          // refill the stage of k-tile kt - 1
+      issue_tile<BM, BN, BK, WGM, WGN, NST, true>(p, src, kt + NST - 1, smem + ((kt + NST - 1) % NST) * C::STAGE);
+    if (kt + 1 < nk)
+      decode_tile<BM, BN, BK, WGM, WGN, NST, true>(smem + ((kt + 1) % NST) * C::STAGE,
+                                                   D0 + ((kt + 1) & 1) * (C::BDQ / 16), kt + 1);
+    mma_tile<BM, BN, BK, WGM, WGN, NST, true>(reinterpret_cast<const uint4*>(smem + (kt % NST) * C::STAGE),
+                                              D0 + (kt & 1) * (C::BDQ / 16), acc);
   }
-#undef MOE_DECODE
-#undef MOE_WAIT
-#undef MOE_ISSUE
-  bar_lds();   // every wave is done with the stages before the next tile's loads land
+  epilogue_tile<BM, BN, BK, WGM, WGN, NST, true, EPI>(p, g, r0, r1, n0, nullptr, acc);
+}
 
-  // epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
-  // col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
-  const float gs = (FP4 && p.b_gscale) ? p.b_gscale[g] : 1.0f;
+// Operand fragments of one 16-wide k substep for one wavefront.
+template <class C>
+struct Frags {
+  bf16x8 a[C::TM], b[C::TN];
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int NST>
+__device__ __forceinline__ void read_frags(const char* stage, int s,
+                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, false>>& f) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, false>;
+  constexpr int CPR = C::CPR, WM = C::WM, WN = C::WN;
+  const uint4* As = reinterpret_cast<const uint4*>(stage);
+  const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int ch = s * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int row = r0 + wm * WM + i * 32 + (lane & 31);
-    if (row >= r1) continue;
-    float rsc = gs;
-    if (EPI == EPI_GATE_BF16) rsc *= p.row_scale[row];
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * WM + i * 32 + (lane & 31);
+    f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
+  }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (col >= p.N) continue;
-        float v0 = acc[j][i][4 * q + 0], v1 = acc[j][i][4 * q + 1];
-        float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
-        const int64_t o = (int64_t)row * p.ldc + col;
-        if (EPI == EPI_SQRELU_BF16) {
-          v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
-          v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
-          v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
-        } else {
-          v0 *= rsc; v1 *= rsc; v2 *= rsc; v3 *= rsc;
-        }
-        if (EPI == EPI_F32) {
-          *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
-        } else if (EPI == EPI_Z) {
-          *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
-          *reinterpret_cast<uint2*>((uint16_t*)p.C2 + (int64_t)row * p.ldc2 + col) =
-              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-        } else {
-          if (EPI == EPI_BF16_ADD) {
-            const float4 ad = *reinterpret_cast<const float4*>(p.add + (int64_t)row * p.ld_add + col);
-            v0 += ad.x; v1 += ad.y; v2 += ad.z; v3 += ad.w;
-          }
-          *reinterpret_cast<uint2*>((uint16_t*)p.C + o) =
-              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-        }
-      }
-    }
+  for (int j = 0; j < C::TN; ++j) {
+    const int n = wn * WN + j * 32 + (lane & 31);
+    f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
   }
 }
 
-// Persistent kernel over (row tile, column tile) items.  List 0 holds row tiles
-// of height <= BM (p.tiles / n_tiles[0], or the dense row blocks); list 1, when
-// BMS > 0, holds row tiles of height <= BMS (p.tiles2 / n_tiles[1]): the
-// remainders of each expert's rows, processed with a shorter tile.
-template <int BM, int BN, int BMS, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+template <class C>
+__device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+}
+
+// Scheduling constraint for one substep: alternate the next substep's LDS
+// reads with this substep's MFMAs, so each read's latency hides behind MFMAs
+// instead of stalling the wavefront before the first of them.
+template <class C>
+__device__ __forceinline__ void interleave_reads_mfma() {
+  constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+  constexpr int P = NR < NM ? NR : NM;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+  }
+  if constexpr (NR > P) __builtin_amdgcn_sched_group_barrier(0x100, NR - P, 0);
+  if constexpr (NM > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - P, 0);
+}
+
+// bf16 weights: one block's share of one tile list (items first, first +
+// step, ... of the nrt x ntn items).  The direct-to-LDS ring runs continuously
+// across the block's items: the last k-iterations of one item already load the
+// first k-tiles of the next, so its epilogue overlaps those loads and the
+// pipeline never drains between items.  LDS reads are software-pipelined: the
+// fragments of substep s + 1 are read while the MFMAs of substep s run (two
+// register sets), and the one barrier per k-tile sits before the tile's last
+// substep: after it the wavefront reads the next tile's first fragments and
+// refills the stage it has just finished with, while the last MFMAs of the
+// tile execute.  All NST stages hold k-tiles; requires K / BK >= NST.  The
+// waits leave the previous epilogue's stores in flight until a k-tile issued
+// after them is needed.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+__device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, const int4* list,
+                                                 int nrt, int first, int step) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, false>;
+  constexpr int TM = C::TM, TN = C::TN, S = BK / 16;
+  static_assert(S % 2 == 0, "substep 0 of every k-tile uses the first register set");
+  const int ntn = (p.N + BN - 1) / BN;
+  const int total = nrt * ntn;
+  if (first >= total) return;
+  const int nk = p.K / BK;
+
+  wait_vm<0>();   // only this stream's loads are in flight from here on
+  TileSrc<C> cur, nxt;
+  int it = first;
+  {
+    int g, r0, r1, n0;
+    item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
+    make_src<BM, BN, BK, WGM, WGN, NST, false>(p, g, r0, r1, n0, cur);
+  }
+#pragma unroll
+  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, cur, s, smem + s * C::STAGE);
+  int issued = NST;          // k-tiles of this stream issued so far
+  wait_tiles<C::LOADS, NST - 1>(issued - 1);
+  bar();
+  Frags<C> f0, f1;
+  read_frags<BM, BN, BK, WGM, WGN, NST>(smem, 0, f0);
+  int gt = 0;                // k-tiles of this stream consumed so far
+  constexpr int ST = (EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) ? C::EPI_STORES : 0;
+  int st_tile = -1;          // last k-tile issued before the latest epilogue's stores
+
+  for (;;) {
+    const int itn = it + step;
+    const bool has_next = itn < total;
+    int ng = 0, nr0 = 0, nr1 = 0, nn0 = 0;
+    if (has_next) item_coords<BM, BN>(p, list, nrt, ntn, itn, ng, nr0, nr1, nn0);
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sg = gt % NST;
+      const char* st = smem + sg * C::STAGE;
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s) {
+        if (s % 2 == 0) {
+          read_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f1);
+          mma_frags<C>(f0, acc);
+        } else {
+          read_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f0);
+          mma_frags<C>(f1, acc);
+        }
+        interleave_reads_mfma<C>();
+      }
+      if (kt + 1 < nk || has_next) {
+        // k-tile gt + 1 landed (own loads), own reads of stage sg complete;
+        // after the barrier the same holds for every wavefront
+        wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
+        bar_lds();
+        const int j = kt + NST;          // refill stage sg with the k-tile NST ahead
+        char* fs = smem + sg * C::STAGE;
+        if (j < nk) {
+          issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, cur, j, fs);
+          ++issued;
+        } else if (has_next) {
+          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, false>(p, ng, nr0, nr1, nn0, nxt);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, nxt, j - nk, fs);
+          ++issued;
+        }
+        read_frags<BM, BN, BK, WGM, WGN, NST>(smem + ((gt + 1) % NST) * C::STAGE, 0, f0);
+      }
+      // one call site for the last substep: duplicating it in both branches
+      // doubles the live accumulators and spills them
+      mma_frags<C>(f1, acc);
+      interleave_reads_mfma<C>();
+      ++gt;
+    }
+    st_tile = issued - 1;
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, false, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
+                                                         smem + NST * C::STAGE, acc);
+    if (!has_next) break;
+    cur = nxt;
+    it = itn;
+  }
+  bar_lds();   // every wave is done with the LDS before the caller reuses it
+}
+
+// Persistent kernel.  Phase 1 walks list 0 (row tiles of height <= BM, or the
+// dense row blocks), phase 2 list 1 (row tiles of height <= BMS: the remainder
+// of each expert's rows) with its own, deeper k-pipeline.  Block b takes the
+// items of its XCD's slice of each round of gridDim.x items (block b runs on
+// XCD b % 8), so consecutive items (the column tiles of one row tile, then the
+// next row tiles of the same expert) share an L2.
+template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, bool FP4,
+          int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   extern __shared__ uint4 smem_u4[];
   char* smem = reinterpret_cast<char*>(smem_u4);
-  const int ntn = (p.N + BN - 1) / BN;
-  const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
-  const int nrt1 = BMS > 0 ? p.n_tiles[1] : 0;
-  const int items0 = nrt0 * ntn;
-  const int total = items0 + nrt1 * ntn;
-  // Consecutive items (the column tiles of one row tile, then the next row
-  // tiles of the same expert) go to blocks of the same XCD, which share an L2:
-  // block b runs on XCD b % 8, so it takes the items of slice b % 8 of each
-  // round of gridDim.x items.
   const int G = gridDim.x;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = G >> 3;
-  const int base = (G & 7) == 0 ? xcd * per_xcd + slot : blockIdx.x;
-  for (int round = 0; round * G < total; ++round) {
-    const int item = round * G + base;
-    if (item >= total) continue;
-    int it = item;
-    const int4* list = p.tiles;
-    if (it >= items0) { it -= items0; list = p.tiles2; }
-    int rt = it / ntn, nt = it - rt * ntn;
-    if (!list && ntn > 8) {
-      // dense and wide: walk bands of 4 row tiles column by column, so the 32
-      // consecutive items of one XCD reuse 4 A and 8 B strips from its L2
-      const int band = it / (4 * ntn), in = it - band * 4 * ntn;
-      const int rows = min(4, nrt0 - band * 4);
-      rt = band * 4 + in % rows;
-      nt = in / rows;
-    }
-    int g = 0, r0, r1;
-    if (list) {
-      const int4 tl = list[rt];
-      g = tl.x; r0 = tl.y; r1 = tl.z;
-    } else {
-      r0 = rt * BM; r1 = min(p.M, r0 + BM);
-    }
-    if constexpr (BMS > 0) {
-      if (item >= items0) {
-        gemm_tile<BMS, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
-        continue;
+  const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
+  if constexpr (FP4) {
+    // one item space over both lists, dealt round-robin: each block gets the
+    // same number of items (to one), remainder tiles filling the last round
+    // of full tiles
+    const int ntn = (p.N + BN - 1) / BN;
+    const int items0 = nrt0 * ntn;
+    const int total = items0 + (BMS > 0 ? p.n_tiles[1] * ntn : 0);
+    for (int it = base; it < total; it += G) {
+      if (BMS > 0 && it >= items0) {
+        int g, r0, r1, n0;
+        item_coords<(BMS > 0 ? BMS : BM), BN>(p, p.tiles2, p.n_tiles[1], ntn, it - items0, g, r0, r1, n0);
+        fp4_tile<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, EPI>(p, smem, g, r0, r1, n0);
+      } else {
+        int g, r0, r1, n0;
+        item_coords<BM, BN>(p, p.tiles, nrt0, ntn, it, g, r0, r1, n0);
+        fp4_tile<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, g, r0, r1, n0);
       }
     }
-    gemm_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, smem, g, r0, r1, nt * BN);
+  } else {
+    gemm_stream_bf16<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
+    if constexpr (BMS > 0)
+      gemm_stream_bf16<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
   }
 }
 
 namespace {
 
-template <int BM, int BN, int BMS, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, bool FP4,
+          int EPI>
 hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t s) {
-  constexpr size_t lds = (size_t)TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::LDS;
+  constexpr size_t lds1 = (size_t)TileCfg<BM, BN, BK1, WGM, WGN, NST1, FP4>::LDS;
+  constexpr size_t lds2 = BMS > 0 ? (size_t)TileCfg<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, FP4>::LDS : 0;
+  constexpr size_t lds = lds1 > lds2 ? lds1 : lds2;
   static_assert(lds <= 160 * 1024, "LDS");
-  auto* kern = gemm_bf16_kernel<BM, BN, BMS, BK, WGM, WGN, NST, FP4, EPI>;
+  auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, FP4, EPI>;
+  // k-tiles per output tile: NVFP4 streams fill NST - 1 stages ahead, bf16 ones all NST
+  constexpr int need1 = FP4 ? NST1 - 1 : NST1, need2 = FP4 ? NST2 - 1 : NST2;
+  if (a.K / BK1 < need1 || (BMS > 0 && a.K / BK2 < need2)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -408,33 +738,45 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
   return hipGetLastError();
 }
 
-// bf16: BK = 64 (fewer barriers per flop) with 2 stages for 256x256 tiles
-// and 3 for the smaller ones.  NVFP4: BK = 32 with a 4-stage ring; the codes and
-// scales are staged raw and decoded in LDS one k-tile ahead of the MFMAs.
+// bf16: both lists with BK = 64 (fewer barriers per flop; 2 stages for
+// 256x256 tiles, 3 for smaller ones).  NVFP4: BK = 32 with a 4-stage
+// ring; codes and scales are staged raw and decoded in LDS one k-tile ahead of
+// the MFMAs.  Short reductions (K = 64, 128) take rings that fit in K / BK
+// k-tiles.
+template <int BM, int BN, int BMS, int WGM, int WGN, int EPI, bool GROUPED>
+hipError_t launch_epi(const GemmArgs& a, bool fp4, int64_t grid, int num_cu, hipStream_t s) {
+  constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
+  if constexpr (GROUPED) {         // NVFP4 weights: grouped expert GEMMs only
+    if (fp4) {
+      if (a.K >= 128) return launch_one<BM, BN, BMS, WGM, WGN, 32, 5, 32, 5, true, EPI>(a, grid, num_cu, s);
+      return launch_one<BM, BN, BMS, WGM, WGN, 32, 3, 32, 3, true, EPI>(a, grid, num_cu, s);
+    }
+  }
+  if (fp4) return hipErrorInvalidValue;
+  if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, NSTB, 64, NSTB, false, EPI>(a, grid, num_cu, s);
+  if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 32, 4, 32, 4, false, EPI>(a, grid, num_cu, s);
+  return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, false, EPI>(a, grid, num_cu, s);
+}
+
 template <int BM, int BN, int BMS, int WGM, int WGN>
 hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int num_cu, hipStream_t s) {
-  constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
-  if (fp4) {
-    if (a.tiles) {              // NVFP4 is used for the grouped expert GEMMs only
+  if (a.tiles) {                   // grouped expert GEMMs: bf16 or NVFP4 weights
+    if constexpr (BMS > 0) {
       switch (epi) {
-        case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_SQRELU_BF16>(a, grid, num_cu, s);
-        case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 32, WGM, WGN, 4, true, EPI_GATE_BF16>(a, grid, num_cu, s);
+        case EPI_SQRELU_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_SQRELU_BF16, true>(a, fp4, grid, num_cu, s);
+        case EPI_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_BF16, true>(a, fp4, grid, num_cu, s);
         default: break;
       }
     }
     return hipErrorInvalidValue;
   }
+  if (fp4 || BMS != 0) return hipErrorInvalidValue;   // dense GEMMs: bf16 weights, no lists
   switch (epi) {
-    case EPI_SQRELU_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, NSTB, false, EPI_SQRELU_BF16>(a, grid, num_cu, s);
-    case EPI_GATE_BF16: return launch_one<BM, BN, BMS, 64, WGM, WGN, NSTB, false, EPI_GATE_BF16>(a, grid, num_cu, s);
-    default: break;
-  }
-  if (BMS != 0) return hipErrorInvalidValue;     // dense epilogues have no tile lists
-  switch (epi) {
-    case EPI_BF16: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_BF16>(a, grid, num_cu, s);
-    case EPI_Z: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_Z>(a, grid, num_cu, s);
-    case EPI_F32: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_F32>(a, grid, num_cu, s);
-    case EPI_BF16_ADD: return launch_one<BM, BN, 0, 64, WGM, WGN, NSTB, false, EPI_BF16_ADD>(a, grid, num_cu, s);
+    case EPI_SQRELU_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_SQRELU_BF16, false>(a, false, grid, num_cu, s);
+    case EPI_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16, false>(a, false, grid, num_cu, s);
+    case EPI_Z: return launch_epi<BM, BN, 0, WGM, WGN, EPI_Z, false>(a, false, grid, num_cu, s);
+    case EPI_F32: return launch_epi<BM, BN, 0, WGM, WGN, EPI_F32, false>(a, false, grid, num_cu, s);
+    case EPI_BF16_ADD: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16_ADD, false>(a, false, grid, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -455,9 +797,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, in
     if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
     return hipErrorInvalidValue;
   }
-  if (bm == 256 && bn == 256 && bms == 0) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
   if (bm == 256 && bn == 256 && bms == 128) return launch_shape<256, 256, 128, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
-  if (bm == 256 && bn == 128 && bms == 64) return launch_shape<256, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
   if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
   return hipErrorInvalidValue;
 }

@@ -97,8 +97,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
           } else if (EPI == EPI_SQRELU_F32) {
             v = fmaxf(v, 0.0f);
             *C = v * v;
-          } else if (EPI == EPI_GATE_F32) {
-            *C = p.row_scale[row] * v;
           } else if (EPI == EPI_F32_ADD) {
             *C = v + p.add[(int64_t)row * p.ld_add + col];
           }
@@ -118,7 +116,6 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_
   switch (epi) {
     case EPI_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_F32); else MOE_F32_CASE(false, EPI_F32); break;
     case EPI_SQRELU_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_SQRELU_F32); else MOE_F32_CASE(false, EPI_SQRELU_F32); break;
-    case EPI_GATE_F32: if (a_is_bf16) MOE_F32_CASE(true, EPI_GATE_F32); else MOE_F32_CASE(false, EPI_GATE_F32); break;
     case EPI_F32_ADD: if (a_is_bf16) MOE_F32_CASE(true, EPI_F32_ADD); else MOE_F32_CASE(false, EPI_F32_ADD); break;
     default: return hipErrorInvalidValue;
   }

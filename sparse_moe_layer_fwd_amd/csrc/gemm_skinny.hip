@@ -127,8 +127,6 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
       const int r = rb * 16 + (lane >> 4) * 4 + i;     // D[i = 4*(lane/16) + r][j = lane%16]
       if (r >= cnt) continue;
       const int64_t orow = row0 + r;
-      float rsc = 1.0f;
-      if (EPI == EPI_GATE_BF16) rsc = p.row_scale[orow];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int col = n0 + cb * 16 + (lane & 15);
@@ -141,7 +139,7 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
           const float h = fmaxf(v, 0.0f);
           *C = (uint16_t)f2bf(h * h);
         } else {
-          *C = (uint16_t)f2bf(rsc * v);
+          *C = (uint16_t)f2bf(v);
         }
       }
     }
@@ -168,11 +166,11 @@ hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_exper
   dim3 g((a.N + 63) / 64, n_experts), b(256);
   if (b_nvfp4) {
     if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_SQRELU_BF16>), g, b, 0, s, a);
-    else if (epi == EPI_GATE_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_GATE_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_BF16>), g, b, 0, s, a);
     else return hipErrorInvalidValue;
   } else {
     if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_SQRELU_BF16>), g, b, 0, s, a);
-    else if (epi == EPI_GATE_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_GATE_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_BF16>), g, b, 0, s, a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -91,7 +91,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
   size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
-  size_t slot_token, slot_gate, tk_slot, H, O, u, Hs, ys, total;
+  size_t slot_token, tk_slot, H, O, u, Hs, ys, total;
   int nchunks, bm, bms, max_tiles, max_tiles2;
   int cold;        // prefill: experts with fewer rows go to the skinny kernel (0: none)
   bool f32, skinny;
@@ -148,8 +148,9 @@ Plan make_plan(const moe_config_t& c, int T) {
   p.tiles = take((size_t)p.max_tiles * 16);
   p.tiles2 = take((size_t)p.max_tiles2 * 16);
   p.ntiles = take(8);
-  p.slot_token = take(Tz * K * 4);
-  p.slot_gate = take(Tz * K * 4);
+  // 64 bytes past the end: the tiled GEMM reads a tile's row indices in
+  // aligned groups of up to 16 with scalar loads and discards those past the tile
+  p.slot_token = take(Tz * K * 4 + 64);
   p.tk_slot = take(Tz * K * 4);
   p.H = take(Tz * K * M * es);
   p.O = take(Tz * K * L * es);
@@ -254,7 +255,8 @@ int copy_out(moe_handle_t h, int T, const void* ws, const Plan& p, int32_t* idx,
   return MOE_OK;
 }
 
-// One grouped expert GEMM (up: sqrelu epilogue; down: gate epilogue).
+// One grouped expert GEMM (up: sqrelu epilogue; down: plain, gates are applied by
+// the combine).
 int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const void* A,
                         const int* a_rows, void* C, hipStream_t s) {
   const moe_config_t& c = h->c;
@@ -279,8 +281,7 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   sk.counts = at<int>(ws, p.counts); sk.offs = at<int>(ws, p.offs);
   sk.max_rows = p.skinny ? INT32_MAX : p.cold;
   sk.C = (uint16_t*)C; sk.ldc = rows;
-  sk.row_scale = at<float>(ws, p.slot_gate);
-  const int epi = up ? EPI_SQRELU_BF16 : EPI_GATE_BF16;
+  const int epi = up ? EPI_SQRELU_BF16 : EPI_BF16;
   if (p.skinny) {
     MOE_TRY(launch_skinny(sk, fp4, epi, c.n_experts, s));
     return MOE_OK;
@@ -296,10 +297,9 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   a.tiles = at<int4>(ws, p.tiles); a.n_tiles = at<int>(ws, p.ntiles);
   a.tiles2 = at<int4>(ws, p.tiles2);
   a.C = C; a.ldc = rows;
-  a.row_scale = at<float>(ws, p.slot_gate);
   if (p.f32) {
     a.M = p.max_tiles;   // grouped: upper bound on row tiles (grid sizing)
-    MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_GATE_F32, cap, s));
+    MOE_TRY(launch_gemm_f32(a, false, up ? EPI_SQRELU_F32 : EPI_F32, cap, s));
     return MOE_OK;
   }
   const int bn = p.bm == 256 ? 256 : 128;
@@ -458,9 +458,8 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
   if (st != MOE_OK) return st;
   {
     StageScope sc(MOE_STAGE_SCATTER, s);
-    MOE_TRY(launch_scatter(at<int>(ws, p.idx), at<float>(ws, p.gate), T, c.top_k, c.n_experts,
-                           kTokensPerChunk, at<int>(ws, p.cbase), at<int>(ws, p.offs),
-                           at<int>(ws, p.slot_token), at<float>(ws, p.slot_gate),
+    MOE_TRY(launch_scatter(at<int>(ws, p.idx), T, c.top_k, c.n_experts, kTokensPerChunk,
+                           at<int>(ws, p.cbase), at<int>(ws, p.offs), at<int>(ws, p.slot_token),
                            at<int>(ws, p.tk_slot), s));
   }
   // expert FFNs over expert-sorted rows
@@ -496,8 +495,9 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
   if (c.has_latent_proj) {
     {
       StageScope sc(MOE_STAGE_COMBINE, s);
-      MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot), T,
-                             c.top_k, c.latent, nullptr, at<void>(ws, p.u), p.f32, s));
+      MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot),
+                             at<float>(ws, p.gate), T, c.top_k, c.latent, nullptr, at<void>(ws, p.u),
+                             p.f32, s));
     }
     StageScope sc(MOE_STAGE_UP_PROJ, s);
     GemmArgs a = gemm_args();
@@ -510,8 +510,8 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     else MOE_TRY(dense_bf16(a, ys ? EPI_BF16_ADD : EPI_BF16, h->num_cu, s));
   } else {
     StageScope sc(MOE_STAGE_COMBINE, s);
-    MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot), T, c.top_k,
-                           c.d, ys, y, p.f32, s));
+    MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot),
+                           at<float>(ws, p.gate), T, c.top_k, c.d, ys, y, p.f32, s));
   }
   return copy_out(h, T, ws, p, idx, gate, counts, s);
 }

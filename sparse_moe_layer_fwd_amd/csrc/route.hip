@@ -212,13 +212,11 @@ hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int 
 // handles assignment (t, k).  A token's K experts are distinct, so the K lanes
 // update K different LDS counters: within an expert the slots follow (t, k)
 // order, a stable and deterministic scatter.
-__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx,
-                                                     const float* __restrict__ gate, int T, int K,
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx, int T, int K,
                                                      int N, int tc,
                                                      const int* __restrict__ chunk_base,
                                                      const int* __restrict__ offs,
                                                      int* __restrict__ slot_token,
-                                                     float* __restrict__ slot_gate,
                                                      int* __restrict__ tk_slot) {
   __shared__ int cnt[1024];
   const int c = blockIdx.x, lane = threadIdx.x;
@@ -232,27 +230,27 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx
       const int slot = cnt[e];
       cnt[e] = slot + 1;
       slot_token[slot] = t;
-      slot_gate[slot] = gate[a];
       tk_slot[a] = slot;
     }
   }
 }
 
-hipError_t launch_scatter(const int* idx, const float* gate, int T, int K, int N, int tc,
-                          const int* chunk_base, const int* offs, int* slot_token,
-                          float* slot_gate, int* tk_slot, hipStream_t s) {
+hipError_t launch_scatter(const int* idx, int T, int K, int N, int tc, const int* chunk_base,
+                          const int* offs, int* slot_token, int* tk_slot, hipStream_t s) {
   const int nchunks = (T + tc - 1) / tc;
-  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, idx, gate, T, K, N, tc,
-                     chunk_base, offs, slot_token, slot_gate, tk_slot);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, idx, T, K, N, tc,
+                     chunk_base, offs, slot_token, tk_slot);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ combine
-// out[t][c] = add[t][c] + sum_{k=0..K-1} O[tk_slot[t][k]][c], summed in fp32 in
-// that fixed order (no atomics), then stored once.  8 columns per thread.
+// out[t][c] = add[t][c] + sum_{k=0..K-1} gate[t][k] * O[tk_slot[t][k]][c], summed
+// in fp32 in that fixed order (no atomics), then stored once.  8 columns per
+// thread.
 template <bool OF32, bool OUTF32>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O, int64_t ldo,
-                                                      const int* __restrict__ tk_slot, int K, int W,
+                                                      const int* __restrict__ tk_slot,
+                                                      const float* __restrict__ gate, int K, int W,
                                                       const float* __restrict__ add,
                                                       void* __restrict__ out) {
   const int t = blockIdx.x;
@@ -269,19 +267,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   }
   const int* sl = tk_slot + (int64_t)t * K;
+  const float* gl = gate + (int64_t)t * K;
   for (int k = 0; k < K; ++k) {
     const int64_t s = sl[k];
+    const float g = gl[k];
     if (OF32) {
       const float4* p = reinterpret_cast<const float4*>((const float*)O + s * ldo + c0);
       float4 a = p[0], b = p[1];
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      acc[0] += g * a.x; acc[1] += g * a.y; acc[2] += g * a.z; acc[3] += g * a.w;
+      acc[4] += g * b.x; acc[5] += g * b.y; acc[6] += g * b.z; acc[7] += g * b.w;
     } else {
       const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)O + s * ldo + c0);
-      acc[0] += bf2f(v.x & 0xFFFFu); acc[1] += bf2f(v.x >> 16);
-      acc[2] += bf2f(v.y & 0xFFFFu); acc[3] += bf2f(v.y >> 16);
-      acc[4] += bf2f(v.z & 0xFFFFu); acc[5] += bf2f(v.z >> 16);
-      acc[6] += bf2f(v.w & 0xFFFFu); acc[7] += bf2f(v.w >> 16);
+      acc[0] += g * bf2f(v.x & 0xFFFFu); acc[1] += g * bf2f(v.x >> 16);
+      acc[2] += g * bf2f(v.y & 0xFFFFu); acc[3] += g * bf2f(v.y >> 16);
+      acc[4] += g * bf2f(v.z & 0xFFFFu); acc[5] += g * bf2f(v.z >> 16);
+      acc[6] += g * bf2f(v.w & 0xFFFFu); acc[7] += g * bf2f(v.w >> 16);
     }
   }
   if (OUTF32) {
@@ -296,13 +296,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
   }
 }
 
-hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot, int T, int K,
-                          int W, const float* add, void* out, bool out_f32, hipStream_t s) {
+hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot,
+                          const float* gate, int T, int K, int W, const float* add, void* out,
+                          bool out_f32, hipStream_t s) {
   dim3 g(T, (W + 2047) / 2048), b(256);
-  if (o_f32 && out_f32) hipLaunchKernelGGL((combine_kernel<true, true>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
-  else if (o_f32) hipLaunchKernelGGL((combine_kernel<true, false>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
-  else if (out_f32) hipLaunchKernelGGL((combine_kernel<false, true>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
-  else hipLaunchKernelGGL((combine_kernel<false, false>), g, b, 0, s, O, ldo, tk_slot, K, W, add, out);
+  if (o_f32 && out_f32) hipLaunchKernelGGL((combine_kernel<true, true>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
+  else if (o_f32) hipLaunchKernelGGL((combine_kernel<true, false>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
+  else if (out_f32) hipLaunchKernelGGL((combine_kernel<false, true>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
+  else hipLaunchKernelGGL((combine_kernel<false, false>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
   return hipGetLastError();
 }
 

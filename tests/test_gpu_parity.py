@@ -104,14 +104,27 @@ SMALL = {
     "k_equals_n": MoEConfig("k_equals_n", T=90, d=256, latent=128, n_experts=6, top_k=6, ffn=128),
     "many_experts_small_batch": MoEConfig("many_experts_small_batch", T=70, d=256, latent=128,
                                           n_experts=1000, top_k=12, ffn=128),
-    # T*K >= 256*N: hot experts on 256-row tiles, cold experts on the skinny kernel
+    # T*K >= 256*N: 256-row tiles, each expert's remaining rows on 128-row tiles
     "hot_cold_bf16": MoEConfig("hot_cold_bf16", T=600, d=512, latent=256, n_experts=8, top_k=4,
                                ffn=256, zipf_s=1.1),
     "hot_cold_nvfp4": MoEConfig("hot_cold_nvfp4", T=700, d=512, latent=256, n_experts=8, top_k=4,
                                 ffn=512, expert="nvfp4", zipf_s=1.1),
-    # same regime with l not a multiple of 256: every expert on 256-row tiles
+    # same regime with l not a multiple of 256
     "big_tiles_no_cold": MoEConfig("big_tiles_no_cold", T=600, d=256, latent=192, n_experts=8,
                                    top_k=4, ffn=128, zipf_s=1.1),
+    # K = 64 reductions (latent and ffn): the shortest k-pipelines
+    "short_k_bf16": MoEConfig("short_k_bf16", T=300, d=256, latent=64, n_experts=8, top_k=2,
+                              ffn=64),
+    "short_k_nvfp4_big_tiles": MoEConfig("short_k_nvfp4_big_tiles", T=600, d=256, latent=64,
+                                         n_experts=4, top_k=4, ffn=64, expert="nvfp4"),
+    # more output tiles than the persistent grid has blocks: each block runs
+    # several tiles back to back through one continuous load pipeline
+    "multi_item_256": MoEConfig("multi_item_256", T=8192, d=256, latent=256, n_experts=8, top_k=4,
+                                ffn=1024, zipf_s=1.1),
+    "multi_item_128": MoEConfig("multi_item_128", T=2048, d=256, latent=256, n_experts=64, top_k=4,
+                                ffn=1024),
+    "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
+                                  top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
 }
 
 
