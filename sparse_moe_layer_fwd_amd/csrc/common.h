@@ -45,7 +45,8 @@ enum Epi : int {
   EPI_F32 = 4,         // C(f32) = acc (+ bias[col])                  (router, shared down)
   EPI_BF16_ADD = 5,    // C(bf16) = acc + add[r][c] (fp32)            (up-proj + shared)
   EPI_SQRELU_F32 = 6,  // C(f32) = max(acc,0)^2
-  EPI_F32_ADD = 8      // C(f32) = acc + add[r][c]
+  EPI_F32_ADD = 8,     // C(f32) = acc + add[r][c]
+  EPI_PARTIAL = 9      // C(f32)[slice blockIdx.y] = acc over that slice of K (split-K)
 };
 // g: the NVFP4 per-expert global scale (1 for bf16 weights).  Gates are not
 // applied by any GEMM: the combine step multiplies each expert output by its
@@ -76,11 +77,22 @@ struct SkinnyArgs {
   const int* counts; const int* offs;
   int32_t max_rows;                                   // experts with >= max_rows rows are skipped
   uint16_t* C; int64_t ldc;
+  float* P; int64_t p_slice;                          // split-K partials: slice s at P + s * p_slice
 };
 
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s);
+// Dense GEMM with K split into ks slices (ks > 1): partial sums into P
+// (ks * M * N floats), then a fixed-order sum over the slices and epilogue epi.
+// Every dimension of the fp32 kernel: K % (32 * ks) == 0.
+hipError_t launch_gemm_f32_splitk(const GemmArgs& a, bool a_is_bf16, int epi, int ks, float* P,
+                                  hipStream_t s);
+// bf16 dense GEMM with M <= 64 on the skinny kernel, K split into ks slices
+// (K % (256 * ks) == 0, N % 64 == 0), then the same sum and epilogue.
+hipError_t launch_skinny_splitk(const GemmArgs& a, int epi, int ks, float* P, hipStream_t s);
+// out = epi( sum over the ks slices of P ), one thread per output element
+hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float* P, hipStream_t s);
 // num_cu: compute units of the device (the persistent grid is sized from it)
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
                             int64_t max_items, int num_cu, hipStream_t s);

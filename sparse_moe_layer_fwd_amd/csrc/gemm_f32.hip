@@ -40,7 +40,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < p.K; k0 += BK) {
+    // split-K (EPI_PARTIAL): slice blockIdx.y of gridDim.y covers K / gridDim.y
+    const int kl = EPI == EPI_PARTIAL ? p.K / (int)gridDim.y : p.K;
+    const int kb = EPI == EPI_PARTIAL ? (int)blockIdx.y * kl : 0;
+    for (int k0 = kb; k0 < kb + kl; k0 += BK) {
       float av[8], bv[8];
       if (ABF16) {
         const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)p.A + arow * p.lda + k0 + kq);
@@ -91,7 +94,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
           if (row >= r1 || col >= p.N) continue;
           float v = acc[i][j][r];
           float* C = (float*)p.C + (int64_t)row * p.ldc + col;
-          if (EPI == EPI_F32) {
+          if (EPI == EPI_PARTIAL) {
+            C[(int64_t)blockIdx.y * p.M * p.ldc] = v;
+          } else if (EPI == EPI_F32) {
             if (p.bias) v += p.bias[col];
             *C = v;
           } else if (EPI == EPI_SQRELU_F32) {
@@ -121,6 +126,66 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_
   }
 #undef MOE_F32_CASE
   return hipGetLastError();
+}
+
+// out[r][c] = epi( sum_{s=0..ks-1} P[s][r][c] ), summed in that fixed order.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int ks, int M,
+                                                            int N, GemmArgs p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
+  float v = 0.0f;
+  for (int k = 0; k < ks; ++k) v += P[(int64_t)k * M * N + i];
+  if (EPI == EPI_F32) {
+    if (p.bias) v += p.bias[col];
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = v;
+  } else if (EPI == EPI_F32_ADD) {
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = v + p.add[(int64_t)row * p.ld_add + col];
+  } else if (EPI == EPI_SQRELU_F32) {
+    v = fmaxf(v, 0.0f);
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = v * v;
+  } else if (EPI == EPI_Z) {
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = v;
+    ((uint16_t*)p.C2)[(int64_t)row * p.ldc2 + col] = (uint16_t)f2bf(v);
+  } else if (EPI == EPI_BF16) {
+    ((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(v);
+  } else if (EPI == EPI_BF16_ADD) {
+    ((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(v + p.add[(int64_t)row * p.ld_add + col]);
+  } else if (EPI == EPI_SQRELU_BF16) {
+    v = fmaxf(v, 0.0f);
+    ((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(v * v);
+  }
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float* P, hipStream_t s) {
+  const int64_t n = (int64_t)a.M * a.N;
+  dim3 g((unsigned)((n + 255) / 256)), b(256);
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_F32>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_F32_ADD: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_F32_ADD>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_SQRELU_F32: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SQRELU_F32>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_Z: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_Z>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_BF16: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_BF16_ADD: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16_ADD>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_SQRELU_BF16: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SQRELU_BF16>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32_splitk(const GemmArgs& a, bool a_is_bf16, int epi, int ks, float* P,
+                                  hipStream_t s) {
+  if (a.tiles || ks < 2 || a.K % (32 * ks) != 0) return hipErrorInvalidValue;
+  GemmArgs q = a;
+  q.C = P; q.ldc = a.N; q.bias = nullptr;
+  const int64_t tiles = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
+  dim3 g((unsigned)tiles, (unsigned)ks), b(256);
+  if (a_is_bf16) hipLaunchKernelGGL((gemm_f32_kernel<true, EPI_PARTIAL>), g, b, 0, s, q);
+  else hipLaunchKernelGGL((gemm_f32_kernel<false, EPI_PARTIAL>), g, b, 0, s, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(a, epi, ks, P, s);
 }
 
 }  // namespace moe

@@ -13,6 +13,8 @@
 // 16 activations of each row block, and issues two v_mfma_f32_16x16x32_bf16 per
 // (row block, column block).  Both operands use the same permutation of the
 // reduction index inside a step, which leaves the dot products unchanged.
+#include <string.h>
+
 #include "common.h"
 
 namespace moe {
@@ -26,14 +28,16 @@ __device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
 }  // namespace
 
 // Rows [row0, row0 + cnt) (cnt <= 64) of expert e, columns [n0, n0 + 64).
+// K range [kbeg, kbeg + klen) (klen a multiple of 256): each wavefront takes a
+// quarter.
 template <bool FP4, int EPI>
 __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[16][4][64], int e,
-                                             int row0, int cnt, int n0) {
+                                             int row0, int cnt, int n0, int kbeg, int klen) {
   constexpr int MAXRB = 4;
   const int nrb = (cnt + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kq = p.K >> 2;
-  const int kw0 = wave * kq;
+  const int kq = klen >> 2;
+  const int kw0 = kbeg + wave * kq;
   const int grp = lane >> 4;                             // which 16-wide k slice of a 64-step
   const uint16_t* arow[MAXRB];
 #pragma unroll
@@ -133,6 +137,10 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
         if (col >= p.N) continue;
         float v = acc[rb][cb][i] + red[0][rb * 4 + cb][i][lane] + red[1][rb * 4 + cb][i][lane] +
                   red[2][rb * 4 + cb][i][lane];
+        if (EPI == EPI_PARTIAL) {                        // raw slice sum, K slice blockIdx.y
+          p.P[(int64_t)blockIdx.y * p.p_slice + orow * p.N + col] = v;
+          continue;
+        }
         v *= gs;
         uint16_t* C = p.C + orow * p.ldc + col;
         if (EPI == EPI_SQRELU_BF16) {
@@ -157,9 +165,35 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   if (cnt == 0 || cnt >= p.max_rows) return;
   const int row0 = p.offs[e];
   for (int c0 = 0; c0 < cnt; c0 += 64) {
-    skinny_chunk<FP4, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64);
+    skinny_chunk<FP4, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
     __syncthreads();
   }
+}
+
+// Dense split-K: grid (N / 64, ks, row chunks of 64).  Block (x, y, z) sums
+// rows [64 z, 64 z + 64) x columns [64 x, 64 x + 64) over K slice y into the
+// fp32 partials P[y].
+__global__ __launch_bounds__(256) void skinny_dense_kernel(SkinnyArgs p, int M) {
+  __shared__ float red[3][16][4][64];
+  const int kl = p.K / (int)gridDim.y;
+  const int row0 = blockIdx.z * 64;
+  skinny_chunk<false, EPI_PARTIAL>(p, red, 0, row0, min(64, M - row0), blockIdx.x * 64,
+                                   (int)blockIdx.y * kl, kl);
+}
+
+hipError_t launch_skinny_splitk(const GemmArgs& a, int epi, int ks, float* P, hipStream_t s) {
+  if (a.tiles || ks < 1 || a.K % (256 * ks) != 0 || a.N % 64 != 0 || a.kseg < a.K) return hipErrorInvalidValue;
+  SkinnyArgs k;
+  memset(&k, 0, sizeof(k));
+  k.A = (const uint16_t*)a.A; k.lda = a.lda; k.a_rows = nullptr;
+  k.B = a.B; k.ldb = a.ldb; k.b_gstride = 0;
+  k.N = a.N; k.K = a.K;
+  k.P = P; k.p_slice = (int64_t)a.M * a.N;
+  dim3 g(a.N / 64, ks, (a.M + 63) / 64), b(256);
+  hipLaunchKernelGGL(skinny_dense_kernel, g, b, 0, s, k, a.M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(a, epi, ks, P, s);
 }
 
 hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s) {

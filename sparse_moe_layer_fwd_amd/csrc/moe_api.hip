@@ -36,6 +36,8 @@ constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
 constexpr int kSmallBM = 64;          // grouped bf16 GEMM: height of each expert's remainder tiles
 constexpr int kSmallBM256 = 128;      // ... when the full tiles are 256 rows high
 constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path
+// split-K partial buffer: floats per CU (two blocks of 64 x 64 outputs)
+constexpr size_t kPartialPerCu = 2 * 64 * 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -91,7 +93,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
   size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
-  size_t slot_token, tk_slot, H, O, u, Hs, ys, total;
+  size_t slot_token, tk_slot, H, O, u, Hs, ys, partial, total;
   int nchunks, bm, bms, max_tiles, max_tiles2;
   int cold;        // prefill: experts with fewer rows go to the skinny kernel (0: none)
   bool f32, skinny;
@@ -103,7 +105,7 @@ bool use_skinny(const moe_config_t& c, int T) {
   return !use_f32(c) && T <= kSkinnyMaxT && c.latent % 256 == 0 && c.ffn % 256 == 0;
 }
 
-Plan make_plan(const moe_config_t& c, int T) {
+Plan make_plan(const moe_config_t& c, int T, int num_cu) {
   Plan p;
   memset(&p, 0, sizeof(p));
   const size_t Tz = (size_t)T, N = (size_t)c.n_experts, K = (size_t)c.top_k;
@@ -157,6 +159,9 @@ Plan make_plan(const moe_config_t& c, int T) {
   p.u = take(c.has_latent_proj ? Tz * L * es : 0);
   p.Hs = take(c.n_shared ? Tz * (size_t)c.n_shared * c.shared_ffn * es : 0);
   p.ys = take(c.n_shared ? Tz * D * 4 : 0);
+  // split-K partial sums of the dense GEMMs whose output tiles cannot fill the
+  // device (small batches); the split factors keep them within this bound
+  p.partial = take(kPartialPerCu * (size_t)num_cu * 4);
   p.total = o;
   return p;
 }
@@ -172,10 +177,39 @@ void dense_shape(int M, int N, int num_cu, int* bm, int* bn) {
   else { *bm = 128; *bn = 128; }
 }
 
-hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, hipStream_t s) {
+// K-split factor for an output of `tiles` tiles: the largest power of two
+// that keeps tiles * ks within two blocks per CU, with K divisible by
+// kstep * ks and slices of at least min_slice.  1 when the tiles alone fill
+// the device.  tiles * ks <= 2 * num_cu bounds the partial sums.
+int split_factor(int64_t tiles, int K, int kstep, int min_slice, int num_cu) {
+  if (tiles >= num_cu) return 1;
+  int ks = 1;
+  while (tiles * ks * 2 <= 2 * (int64_t)num_cu && K % (kstep * ks * 2) == 0 && K / (ks * 2) >= min_slice)
+    ks *= 2;
+  return ks;
+}
+
+// Dense bf16 GEMM.  Small batches (M <= 64) run on the skinny kernel with K
+// split across blocks (weights streamed by every CU); larger ones on the
+// largest tile that still gives every CU work.
+hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, float* P, hipStream_t s) {
+  if (a.M <= 64 && a.N % 64 == 0 && a.K % 256 == 0 && a.kseg >= a.K) {
+    const int ks = split_factor(a.N / 64, a.K, 256, 256, num_cu);
+    if ((size_t)ks * a.M * a.N <= kPartialPerCu * (size_t)num_cu)   // always, unless N is huge
+      return launch_skinny_splitk(a, epi, ks, P, s);
+  }
   int bm, bn;
   dense_shape(a.M, a.N, num_cu, &bm, &bn);
   return launch_gemm_bf16(a, false, epi, bm, bn, 0, 0, num_cu, s);
+}
+
+// Dense fp32 GEMM (the router, and every dense GEMM of an all-fp32 layer),
+// K split across blocks when its 64 x 64 output tiles cannot fill the device.
+hipError_t dense_f32(const GemmArgs& a, bool a_bf16, int epi, int num_cu, float* P, hipStream_t s) {
+  const int64_t tiles = (int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64);
+  const int ks = a.kseg >= a.K ? split_factor(tiles, a.K, 32, 64, num_cu) : 1;
+  if (ks > 1) return launch_gemm_f32_splitk(a, a_bf16, epi, ks, P, s);
+  return launch_gemm_f32(a, a_bf16, epi, num_cu * 2, s);
 }
 
 GemmArgs gemm_args() {
@@ -190,7 +224,7 @@ int check_call(moe_handle_t h, const void* x, int32_t T, void* ws, size_t ws_byt
   if (T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !aligned16(x)) return MOE_ERR_INVALID_ARG;
-  const Plan p = make_plan(h->c, T);
+  const Plan p = make_plan(h->c, T, h->num_cu);
   if (!ws || ws_bytes < p.total) return MOE_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255u) != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -205,7 +239,6 @@ int check_call(moe_handle_t h, const void* x, int32_t T, void* ws, size_t ws_byt
 int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& p, hipStream_t s) {
   const moe_config_t& c = h->c;
   const moe_weights_t& w = h->w;
-  const int cap = h->num_cu * 2;
   if (c.has_latent_proj) {
     StageScope sc(MOE_STAGE_DOWN_PROJ, s);
     GemmArgs a = gemm_args();
@@ -214,10 +247,10 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
     a.M = T; a.N = c.latent; a.K = c.d;
     a.C = at<void>(ws, p.z32); a.ldc = c.latent;
     if (p.f32) {
-      MOE_TRY(launch_gemm_f32(a, false, EPI_F32, cap, s));
+      MOE_TRY(dense_f32(a, false, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
     } else {
       a.C2 = at<void>(ws, p.z16); a.ldc2 = c.latent;
-      MOE_TRY(dense_bf16(a, EPI_Z, h->num_cu, s));
+      MOE_TRY(dense_bf16(a, EPI_Z, h->num_cu, at<float>(ws, p.partial), s));
     }
   }
   {
@@ -230,7 +263,7 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
     a.C = at<float>(ws, p.logits); a.ldc = c.n_experts;
     a.bias = w.b_router;
     const bool a_bf16 = !c.has_latent_proj && c.act_dtype == MOE_BF16;
-    MOE_TRY(launch_gemm_f32(a, a_bf16, EPI_F32, cap, s));
+    MOE_TRY(dense_f32(a, a_bf16, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
   }
   {
     StageScope sc(MOE_STAGE_TOPK, s);
@@ -381,7 +414,7 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
 
 int moe_workspace_size(moe_handle_t h, int32_t T, size_t* bytes) {
   if (!h || !bytes || T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
-  *bytes = T == 0 ? 0 : make_plan(h->c, T).total;
+  *bytes = T == 0 ? 0 : make_plan(h->c, T, h->num_cu).total;
   return MOE_OK;
 }
 
@@ -436,7 +469,7 @@ int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gat
   if (!idx || !gate || !counts || !aligned16(idx) || !aligned16(gate) || !aligned16(counts))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  const Plan p = make_plan(h->c, T);
+  const Plan p = make_plan(h->c, T, h->num_cu);
   st = enqueue_routing(h, x, T, ws, p, s);
   if (st != MOE_OK) return st;
   return copy_out(h, T, ws, p, idx, gate, counts, s);
@@ -452,8 +485,7 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
   hipStream_t s = (hipStream_t)stream;
   const moe_config_t& c = h->c;
   const moe_weights_t& w = h->w;
-  const Plan p = make_plan(c, T);
-  const int cap = h->num_cu * 2;
+  const Plan p = make_plan(c, T, h->num_cu);
   st = enqueue_routing(h, x, T, ws, p, s);
   if (st != MOE_OK) return st;
   {
@@ -480,16 +512,16 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     a.B = w.ws1; a.ldb = c.d;
     a.M = T; a.N = sm; a.K = c.d;
     a.C = at<void>(ws, p.Hs); a.ldc = sm;
-    if (p.f32) MOE_TRY(launch_gemm_f32(a, false, EPI_SQRELU_F32, cap, s));
-    else MOE_TRY(dense_bf16(a, EPI_SQRELU_BF16, h->num_cu, s));
+    if (p.f32) MOE_TRY(dense_f32(a, false, EPI_SQRELU_F32, h->num_cu, at<float>(ws, p.partial), s));
+    else MOE_TRY(dense_bf16(a, EPI_SQRELU_BF16, h->num_cu, at<float>(ws, p.partial), s));
     GemmArgs b = gemm_args();
     b.A = at<void>(ws, p.Hs); b.lda = sm;
     b.B = w.ws2; b.ldb = c.shared_ffn;
     b.kseg = c.shared_ffn; b.b_segstride = (int64_t)c.d * c.shared_ffn;
     b.M = T; b.N = c.d; b.K = sm;
     b.C = at<float>(ws, p.ys); b.ldc = c.d;
-    if (p.f32) MOE_TRY(launch_gemm_f32(b, false, EPI_F32, cap, s));
-    else MOE_TRY(dense_bf16(b, EPI_F32, h->num_cu, s));
+    if (p.f32) MOE_TRY(dense_f32(b, false, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
+    else MOE_TRY(dense_bf16(b, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
     ys = at<float>(ws, p.ys);
   }
   if (c.has_latent_proj) {
@@ -506,8 +538,8 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
     a.M = T; a.N = c.d; a.K = c.latent;
     a.C = y; a.ldc = c.d;
     a.add = ys; a.ld_add = c.d;
-    if (p.f32) MOE_TRY(launch_gemm_f32(a, false, ys ? EPI_F32_ADD : EPI_F32, cap, s));
-    else MOE_TRY(dense_bf16(a, ys ? EPI_BF16_ADD : EPI_BF16, h->num_cu, s));
+    if (p.f32) MOE_TRY(dense_f32(a, false, ys ? EPI_F32_ADD : EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
+    else MOE_TRY(dense_bf16(a, ys ? EPI_BF16_ADD : EPI_BF16, h->num_cu, at<float>(ws, p.partial), s));
   } else {
     StageScope sc(MOE_STAGE_COMBINE, s);
     MOE_TRY(launch_combine(at<void>(ws, p.O), p.f32, c.latent, at<int>(ws, p.tk_slot),
