@@ -28,7 +28,7 @@ METRIC = "LatentMoE layer tokens/sec on 1 MI355X; % MFMA peak (prefill), % HBM B
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-CPU_SAMPLE = {1: 64, 2: 256, 3: 512, 4: 64, 5: 96}
+CPU_SAMPLE = {1: 64, 2: 768, 3: 1536, 4: 64, 5: 192}
 
 
 def log(msg):
@@ -40,6 +40,20 @@ def expert_weight_bytes_per_matrix(cfg):
     if cfg.expert == "nvfp4":
         return el / 2 + el / 16 + 4
     return el * (4 if cfg.expert == "f32" else 2)
+
+
+def layer_bytes(cfg, touched):
+    """Algorithmic HBM bytes of one layer step: both weight matrices of every
+    touched expert, the projection, router and shared-expert weights, x and y.
+    Intermediates (latent rows, expert-sorted rows, logits) are not counted."""
+    act = 4 if cfg.act == "f32" else 2
+    b = 2 * touched * expert_weight_bytes_per_matrix(cfg)
+    if cfg.has_latent_proj:
+        b += 2 * cfg.d * cfg.latent * act
+    b += cfg.n_experts * cfg.latent * 4 + cfg.n_experts * 4
+    b += 2 * cfg.n_shared * cfg.shared_ffn * cfg.d * act
+    b += 2 * cfg.T * cfg.d * act
+    return b
 
 
 def measured_traffic(workload):
@@ -209,6 +223,9 @@ def main():
                    "zipf_s": cfg.zipf_s, "experts_touched": touched,
                    "max_rows_per_expert": int(counts_np.max()), "parallelism": "single GPU"},
         "layer_tflops": round(cfg.flops() / (ms_step * 1e-3) / 1e12, 2),
+        # whole-layer HBM fraction (algorithmic bytes / step time / 8 TB/s), the
+        # decode-regime figure
+        "layer_hbm_frac": round(layer_bytes(cfg, touched) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in stages.items() if v[0]},
         "roofline": roof,
     }
