@@ -8,9 +8,10 @@
 // rows can be gathered through a row map (the expert up GEMM reads latent rows
 // straight from z by token id).  B is bf16 or NVFP4: NVFP4 codes (E2M1 values,
 // 16-element E4M3 block scales, FP32 global scale; Korean Nemotron 3 summary,
-// section 2.4 NVFP4 Training) are decoded exactly to bf16 inside LDS once per
-// block and k-tile (every e2m1*e4m3 product is a bf16 value); the global scale
-// multiplies the fp32 accumulator in the epilogue.
+// section 2.4 NVFP4 Training) are staged raw in LDS and decoded exactly to bf16
+// in registers by each wavefront right before its MFMAs (every e2m1*e4m3
+// product is a bf16 value); the global scale multiplies the fp32 accumulator in
+// the epilogue.
 //
 // Data movement: operands go global -> LDS with gfx950's direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
@@ -25,8 +26,8 @@
 //
 // Tile BM x BN, WGM x WGN wavefronts, each owning (BM/WGM) x (BN/WGN) in 32x32
 // MFMA blocks.  The MFMA computes C^T (weights as the A operand, activations as
-// the B operand) so each lane holds 4 consecutive output columns of one row:
-// 8- or 16-byte stores.
+// the B operand) so each lane holds 4 consecutive output columns of one row;
+// bf16 outputs are transposed through LDS before they are stored.
 #include "common.h"
 
 namespace moe {
@@ -97,6 +98,7 @@ __device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
 struct TileCfg {
+  static constexpr bool IS_FP4 = FP4;
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per bf16 row
   static constexpr int A_BYTES = BM * BK * 2;
@@ -104,11 +106,8 @@ struct TileCfg {
   static constexpr int BS_BYTES = BN * 4;                      // NVFP4 scales: one aligned dword per row
   static constexpr int B_BYTES = FP4 ? BQ_BYTES + BS_BYTES : BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int BDQ = FP4 ? BN * BK * 2 : 0;            // decoded B (double-buffered)
-  // bf16 weights: epilogue staging, one 32-row block per wavefront row (NVFP4
-  // tiles spend that LDS on a deeper ring and store directly)
-  static constexpr int EPB = FP4 ? 0 : 32 * WGM * BN * 2;
-  static constexpr int LDS = NST * STAGE + 2 * BDQ + EPB;
+  static constexpr int EPB = 32 * WGM * BN * 2;                // epilogue staging: one 32-row block per wave row
+  static constexpr int LDS = NST * STAGE + EPB;
   static constexpr int A_TOT = BM * CPR / 64;                  // 1 KB DMA blocks per k-tile
   static constexpr int B_TOT = FP4 ? BQ_BYTES / 1024 : BN * CPR / 64;
   static constexpr int S_TOT = FP4 ? BS_BYTES / 256 : 0;       // dword-per-lane DMA blocks
@@ -126,8 +125,6 @@ struct TileCfg {
   static constexpr int EPI_STORES = TM * (32 * WGM * (BN / 8)) / NT;
   static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
-  // NVFP4 decodes k-tile t + 1 while the ring refills the stage of t - 1
-  static_assert(!FP4 || NST >= 3, "NVFP4 ring");
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -251,9 +248,11 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
 #pragma unroll
   for (int j = 0; j < C::B_PW; ++j) {
     const int blk = (wave + j * NW) % C::B_TOT;
-    if (FP4) {                                     // BK/32 chunks of codes per row, unswizzled
-      constexpr int QPR = BK / 32;
-      const int q = blk * 64 + lane, row = q / QPR, pos = q % QPR;
+    if (FP4) {
+      // codes: 16 bytes (32 k) per DMA chunk, stored chunk-major in LDS
+      // ([32-k chunk][row][16 B]) so that the 32 rows of a fragment read hit
+      // 16 banks at most twice
+      const int q = blk * 64 + lane, row = q % BN, pos = q / BN;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
       s.boff[j] = n * (uint32_t)p.ldb + pos * 16;  // bytes
     } else {
@@ -310,61 +309,6 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
   }
 }
 
-// NVFP4: decode the raw codes of k-tile kt (its position inside its tile's K
-// loop) from `stage` into the bf16 buffer D.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
-__device__ __forceinline__ void decode_tile(const char* stage, uint4* D, int kt) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
-  constexpr int CPR = C::CPR;
-  const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
-  const uint8_t* Sc = Q + C::BQ_BYTES;
-  constexpr int UNITS = BN * BK / 16;              // one 16-code block per unit
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u0 = 0; u0 < UNITS; u0 += C::NT) {
-    const int u = u0 + tid;
-    if (UNITS % C::NT == 0 || u < UNITS) {
-      const int row = u / (BK / 16), blk = u % (BK / 16);
-      const uint2 q = *reinterpret_cast<const uint2*>(Q + row * (BK / 2) + blk * 8);
-      const Fp4Scale sc = split_scale(Sc[row * 4 + ((kt * (BK / 16)) & 3) + blk]);
-      D[row * CPR + swz_chunk<CPR>(row, 2 * blk + 0)] = fp4x8(q.x, sc);
-      D[row * CPR + swz_chunk<CPR>(row, 2 * blk + 1)] = fp4x8(q.y, sc);
-    }
-  }
-}
-
-// acc += A_stage * B_stage^T for one k-tile (the MFMA computes C^T: weights as
-// its A operand, activations as its B operand).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
-__device__ __forceinline__ void mma_tile(
-    const uint4* As, const uint4* Bs,
-    f32x16 (&acc)[TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TN][TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TM]) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
-  constexpr int CPR = C::CPR, TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-#pragma unroll
-  for (int s = 0; s < BK / 16; ++s) {
-    const int ch = s * 2 + (lane >> 5);
-    bf16x8 a[TM], b[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WM + i * 32 + (lane & 31);
-      a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = wn * WN + j * 32 + (lane & 31);
-      b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[j][i], 0, 0, 0);
-  }
-}
-
 // Epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
 // col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
 // bf16 outputs go through LDS (`stage`, EPB bytes): a lane's own values cover
@@ -381,7 +325,7 @@ __device__ __forceinline__ void epilogue_tile(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const float gs = (FP4 && p.b_gscale) ? sload(p.b_gscale + g) : 1.0f;
-  if constexpr ((EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) && !FP4) {
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) {
     constexpr int U = BN / 8;                      // 16-byte units per staged row
     constexpr int ROWS = 32 * WGM;                 // staged rows per i-block
     constexpr int PER = ROWS * U / C::NT;          // units stored per thread
@@ -467,67 +411,26 @@ __device__ __forceinline__ void epilogue_tile(
   }
 }
 
-// NVFP4 weights: one output tile (rows [r0, r1) of expert g, columns [n0,
-// n0 + BN)).  The raw codes and scales of k-tile t + 1 are decoded into a
-// bf16 buffer (two of them, alternating) while k-tile t is multiplied, so each
-// wait covers the k-tile about to be decoded; the ring keeps NST - 2 further
-// k-tiles in flight.  Every tile restarts the ring (measured faster for these
-// tiles than running it across tiles).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
-__device__ __forceinline__ void fp4_tile(const GemmArgs& p, char* smem, int g, int r0, int r1, int n0) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, true>;
-  constexpr int TM = C::TM, TN = C::TN;
-  const int nk = p.K / BK;                          // >= NST - 1 (checked by the launcher)
-  uint4* D0 = reinterpret_cast<uint4*>(smem + NST * C::STAGE);
-  TileSrc<C> src;
-  make_src<BM, BN, BK, WGM, WGN, NST, true>(p, g, r0, r1, n0, src);
-  bar_lds();     // every wavefront is done with the previous tile's stages
-  wait_vm<0>();  // and its stores: only this tile's loads are counted below
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, true>(p, src, s, smem + s * C::STAGE);
-  wait_tiles<C::LOADS, NST - 2>(NST - 2);           // k-tile 0 landed
-  bar();
-  decode_tile<BM, BN, BK, WGM, WGN, NST, true>(smem, D0, 0);
-
-  f32x16 acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // the raw k-tile decoded in this iteration (kt + 1) must have landed; the
-    // k-tiles issued after it may stay in flight (in-order completion)
-    const int need = kt + 1 < nk ? kt + 1 : kt;
-    const int issued = kt + NST - 1 < nk ? kt + NST - 1 : nk;
-    wait_tiles<C::LOADS, NST - 2>(issued - 1 - need);
-    bar_lds();                                      // stages and decoded buffer kt complete
-    if (kt + NST - 1 < nk)                          // refill the stage of k-tile kt - 1
-      issue_tile<BM, BN, BK, WGM, WGN, NST, true>(p, src, kt + NST - 1, smem + ((kt + NST - 1) % NST) * C::STAGE);
-    if (kt + 1 < nk)
-      decode_tile<BM, BN, BK, WGM, WGN, NST, true>(smem + ((kt + 1) % NST) * C::STAGE,
-                                                   D0 + ((kt + 1) & 1) * (C::BDQ / 16), kt + 1);
-    mma_tile<BM, BN, BK, WGM, WGN, NST, true>(reinterpret_cast<const uint4*>(smem + (kt % NST) * C::STAGE),
-                                              D0 + (kt & 1) * (C::BDQ / 16), acc);
-  }
-  epilogue_tile<BM, BN, BK, WGM, WGN, NST, true, EPI>(p, g, r0, r1, n0, nullptr, acc);
-}
-
-// Operand fragments of one 16-wide k substep for one wavefront.
-template <class C>
+// Operand fragments of one 16-wide k substep for one wavefront.  NVFP4 B
+// fragments stay raw (8 codes and their block scale) until the MFMAs use them.
+template <class C, bool FP4 = C::IS_FP4>
 struct Frags {
   bf16x8 a[C::TM], b[C::TN];
 };
+template <class C>
+struct Frags<C, true> {
+  bf16x8 a[C::TM];
+  uint32_t bq[C::TN], bs[C::TN];
+};
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NST>
-__device__ __forceinline__ void read_frags(const char* stage, int s,
-                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, false>>& f) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, false>;
+// Fragments of substep s of the k-tile in `stage`.  kbyte: position of the
+// k-tile's first scale byte in the aligned scale dword of each row (NVFP4).
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+__device__ __forceinline__ void read_frags(const char* stage, int s, int kbyte,
+                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& f) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
   constexpr int CPR = C::CPR, WM = C::WM, WN = C::WN;
   const uint4* As = reinterpret_cast<const uint4*>(stage);
-  const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int ch = s * 2 + (lane >> 5);
@@ -536,20 +439,41 @@ __device__ __forceinline__ void read_frags(const char* stage, int s,
     const int row = wm * WM + i * 32 + (lane & 31);
     f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
   }
+  if constexpr (FP4) {
+    // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
+    // 8(s & 1) + 4h of 32-k chunk s / 2
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
+    const uint8_t* Sc = Q + C::BQ_BYTES;
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) {
-    const int n = wn * WN + j * 32 + (lane & 31);
-    f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+    for (int j = 0; j < C::TN; ++j) {
+      const int n = wn * WN + j * 32 + (lane & 31);
+      f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
+                                                   ((lane >> 5) << 2));
+      f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
+    }
+  } else {
+    const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int n = wn * WN + j * 32 + (lane & 31);
+      f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+    }
   }
 }
 
+// acc += fragments (the MFMA computes C^T: weights as its A operand).  NVFP4
+// B fragments are decoded here, exactly, to bf16.
 template <class C>
 __device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
+  for (int j = 0; j < C::TN; ++j) {
+    bf16x8 b;
+    if constexpr (C::IS_FP4) b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
+    else b = f.b[j];
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
-      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[j][i], 0, 0, 0);
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
+  }
 }
 
 // Scheduling constraint for one substep: alternate the next substep's LDS
@@ -557,7 +481,7 @@ __device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN
 // instead of stalling the wavefront before the first of them.
 template <class C>
 __device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int NR = C::TM + C::TN, NM = C::TM * C::TN;
+  constexpr int NR = C::TM + (C::IS_FP4 ? 2 : 1) * C::TN, NM = C::TM * C::TN;
   constexpr int P = NR < NM ? NR : NM;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
@@ -568,8 +492,8 @@ __device__ __forceinline__ void interleave_reads_mfma() {
   if constexpr (NM > P) __builtin_amdgcn_sched_group_barrier(0x008, NM - P, 0);
 }
 
-// bf16 weights: one block's share of one tile list (items first, first +
-// step, ... of the nrt x ntn items).  The direct-to-LDS ring runs continuously
+// One block's share of one tile list (items first, first + step, ... of the
+// nrt x ntn items), bf16 or NVFP4 weights.  The direct-to-LDS ring runs continuously
 // across the block's items: the last k-iterations of one item already load the
 // first k-tiles of the next, so its epilogue overlaps those loads and the
 // pipeline never drains between items.  LDS reads are software-pipelined: the
@@ -579,11 +503,13 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 // refills the stage it has just finished with, while the last MFMAs of the
 // tile execute.  All NST stages hold k-tiles; requires K / BK >= NST.  The
 // waits leave the previous epilogue's stores in flight until a k-tile issued
-// after them is needed.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
-__device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, const int4* list,
-                                                 int nrt, int first, int step) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, false>;
+// after them is needed.  NVFP4 stages hold the raw codes and scales; each
+// wavefront decodes the B fragments it multiplies (those of its wavefront
+// column), so the decode runs on the VALU beside the other wavefront's MFMAs.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+__device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const int4* list,
+                                            int nrt, int first, int step) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
   constexpr int TM = C::TM, TN = C::TN, S = BK / 16;
   static_assert(S % 2 == 0, "substep 0 of every k-tile uses the first register set");
   const int ntn = (p.N + BN - 1) / BN;
@@ -597,15 +523,17 @@ __device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, 
   {
     int g, r0, r1, n0;
     item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
-    make_src<BM, BN, BK, WGM, WGN, NST, false>(p, g, r0, r1, n0, cur);
+    make_src<BM, BN, BK, WGM, WGN, NST, FP4>(p, g, r0, r1, n0, cur);
   }
 #pragma unroll
-  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, cur, s, smem + s * C::STAGE);
+  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, cur, s, smem + s * C::STAGE);
   int issued = NST;          // k-tiles of this stream issued so far
   wait_tiles<C::LOADS, NST - 1>(issued - 1);
   bar();
   Frags<C> f0, f1;
-  read_frags<BM, BN, BK, WGM, WGN, NST>(smem, 0, f0);
+  // the aligned scale dword of each row holds k-tile kt's first scale at this byte
+  auto kbyte = [](int kt) { return (kt * (BK / 16)) & 3; };
+  read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(smem, 0, 0, f0);
   int gt = 0;                // k-tiles of this stream consumed so far
   constexpr int ST = (EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) ? C::EPI_STORES : 0;
   int st_tile = -1;          // last k-tile issued before the latest epilogue's stores
@@ -629,10 +557,10 @@ __device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, 
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
         if (s % 2 == 0) {
-          read_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f1);
+          read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(st, s + 1, kbyte(kt), f1);
           mma_frags<C>(f0, acc);
         } else {
-          read_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f0);
+          read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(st, s + 1, kbyte(kt), f0);
           mma_frags<C>(f1, acc);
         }
         interleave_reads_mfma<C>();
@@ -645,14 +573,15 @@ __device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, 
         const int j = kt + NST;          // refill stage sg with the k-tile NST ahead
         char* fs = smem + sg * C::STAGE;
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, cur, j, fs);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, cur, j, fs);
           ++issued;
         } else if (has_next) {
-          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, false>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, false>(p, nxt, j - nk, fs);
+          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, FP4>(p, ng, nr0, nr1, nn0, nxt);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, nxt, j - nk, fs);
           ++issued;
         }
-        read_frags<BM, BN, BK, WGM, WGN, NST>(smem + ((gt + 1) % NST) * C::STAGE, 0, f0);
+        read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(smem + ((gt + 1) % NST) * C::STAGE, 0,
+                                                   kbyte(kt + 1 < nk ? kt + 1 : 0), f0);
       }
       // one call site for the last substep: duplicating it in both branches
       // doubles the live accumulators and spills them
@@ -661,8 +590,8 @@ __device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, 
       ++gt;
     }
     st_tile = issued - 1;
-    epilogue_tile<BM, BN, BK, WGM, WGN, NST, false, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
-                                                         smem + NST * C::STAGE, acc);
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
+                                                       smem + NST * C::STAGE, acc);
     if (!has_next) break;
     cur = nxt;
     it = itn;
@@ -672,7 +601,7 @@ __device__ __forceinline__ void gemm_stream_bf16(const GemmArgs& p, char* smem, 
 
 // Persistent kernel.  Phase 1 walks list 0 (row tiles of height <= BM, or the
 // dense row blocks), phase 2 list 1 (row tiles of height <= BMS: the remainder
-// of each expert's rows) with its own, deeper k-pipeline.  Block b takes the
+// of each expert's rows) with its own ring.  Block b takes the
 // items of its XCD's slice of each round of gridDim.x items (block b runs on
 // XCD b % 8), so consecutive items (the column tiles of one row tile, then the
 // next row tiles of the same expert) share an L2.
@@ -684,29 +613,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   const int G = gridDim.x;
   const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
-  if constexpr (FP4) {
-    // one item space over both lists, dealt round-robin: each block gets the
-    // same number of items (to one), remainder tiles filling the last round
-    // of full tiles
-    const int ntn = (p.N + BN - 1) / BN;
-    const int items0 = nrt0 * ntn;
-    const int total = items0 + (BMS > 0 ? p.n_tiles[1] * ntn : 0);
-    for (int it = base; it < total; it += G) {
-      if (BMS > 0 && it >= items0) {
-        int g, r0, r1, n0;
-        item_coords<(BMS > 0 ? BMS : BM), BN>(p, p.tiles2, p.n_tiles[1], ntn, it - items0, g, r0, r1, n0);
-        fp4_tile<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, EPI>(p, smem, g, r0, r1, n0);
-      } else {
-        int g, r0, r1, n0;
-        item_coords<BM, BN>(p, p.tiles, nrt0, ntn, it, g, r0, r1, n0);
-        fp4_tile<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, g, r0, r1, n0);
-      }
-    }
-  } else {
-    gemm_stream_bf16<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
-    if constexpr (BMS > 0)
-      gemm_stream_bf16<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
-  }
+  gemm_stream<BM, BN, BK1, WGM, WGN, NST1, FP4, EPI>(p, smem, p.tiles, nrt0, base, G);
+  if constexpr (BMS > 0)
+    gemm_stream<BMS, BN, BK2, WGM, WGN, NST2, FP4, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
 }
 
 namespace {
@@ -719,9 +628,8 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
   constexpr size_t lds = lds1 > lds2 ? lds1 : lds2;
   static_assert(lds <= 160 * 1024, "LDS");
   auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, FP4, EPI>;
-  // k-tiles per output tile: NVFP4 streams fill NST - 1 stages ahead, bf16 ones all NST
-  constexpr int need1 = FP4 ? NST1 - 1 : NST1, need2 = FP4 ? NST2 - 1 : NST2;
-  if (a.K / BK1 < need1 || (BMS > 0 && a.K / BK2 < need2)) return hipErrorInvalidValue;
+  // every stage of the ring holds a k-tile of the first output tile
+  if (a.K / BK1 < NST1 || (BMS > 0 && a.K / BK2 < NST2)) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -739,17 +647,17 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
 }
 
 // bf16: both lists with BK = 64 (fewer barriers per flop; 2 stages for
-// 256x256 tiles, 3 for smaller ones).  NVFP4: BK = 32 with a 4-stage
-// ring; codes and scales are staged raw and decoded in LDS one k-tile ahead of
-// the MFMAs.  Short reductions (K = 64, 128) take rings that fit in K / BK
-// k-tiles.
+// 256x256 tiles, 3 for smaller ones).  NVFP4: BK = 64 with 3 stages (a raw
+// stage is 5/8 of a bf16 one).  Short reductions (K = 64, 128) take rings that
+// fit in K / BK k-tiles.
 template <int BM, int BN, int BMS, int WGM, int WGN, int EPI, bool GROUPED>
 hipError_t launch_epi(const GemmArgs& a, bool fp4, int64_t grid, int num_cu, hipStream_t s) {
   constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
   if constexpr (GROUPED) {         // NVFP4 weights: grouped expert GEMMs only
     if (fp4) {
-      if (a.K >= 128) return launch_one<BM, BN, BMS, WGM, WGN, 32, 5, 32, 5, true, EPI>(a, grid, num_cu, s);
-      return launch_one<BM, BN, BMS, WGM, WGN, 32, 3, 32, 3, true, EPI>(a, grid, num_cu, s);
+      if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, 3, 64, 3, true, EPI>(a, grid, num_cu, s);
+      if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 64, 2, 64, 2, true, EPI>(a, grid, num_cu, s);
+      return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, true, EPI>(a, grid, num_cu, s);
     }
   }
   if (fp4) return hipErrorInvalidValue;
