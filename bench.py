@@ -28,7 +28,7 @@ METRIC = "LatentMoE layer tokens/sec on 1 MI355X; % MFMA peak (prefill), % HBM B
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-CPU_SAMPLE = {1: 64, 2: 768, 3: 1536, 4: 64, 5: 192}
+CPU_SAMPLE = {1: 64, 2: 1536, 3: 3072, 4: 64, 5: 384}
 
 
 def log(msg):
