@@ -6,6 +6,7 @@ router, top-K/softmax, expert histogram/scan/scatter, the two grouped expert
 GEMMs, combine and up-projection, all in libmoe.so on HBM-resident inputs.
 
     python bench.py [--config 3] [--steps 20] [--warmup 5] [--gpus 1]
+    python bench.py --paired      # standard vs latent at the ablation shapes
 
 Prints one JSON line.  `value` is tokens/s of the whole layer.  `roofline`
 describes the dominant kernel (the grouped expert GEMMs): its algorithmic
@@ -101,6 +102,89 @@ def cpu_baseline(cfg, seed, sample):
                       "fp64 numpy incl. per-expert weight decode; %.2f s" % (sample, cfg.T, seed, dt)}
 
 
+def time_layer(cfg, cfg_id, seed, steps, warmup):
+    """Build the layer with seeded weights, warm up, then time `steps`
+    back-to-back moe_forward calls on the current stream (inputs resident in
+    HBM) with the library's per-stage timer on."""
+    import torch
+    from sparse_moe_layer_fwd_amd import binding as B
+    from sparse_moe_layer_fwd_amd.layer import DeviceLayer, x_to_device
+    from sparse_moe_layer_fwd_amd.workloads import Workload
+
+    dev = torch.device("cuda:0")
+    log("bench: config %d %s, generating weights" % (cfg_id, cfg.name))
+    t0 = time.perf_counter()
+    wl = Workload(cfg, seed)
+    layer = DeviceLayer.from_workload(wl, device=dev, threads=16)
+    x = x_to_device(wl, dev)
+    y = torch.empty((cfg.T, cfg.d), dtype=layer.act_torch_dtype(), device=dev)
+    ws = layer.new_workspace(cfg.T)
+    torch.cuda.synchronize()
+    log("bench: inputs resident in HBM (%.1f s); warmup %d" % (time.perf_counter() - t0, warmup))
+
+    for _ in range(warmup):
+        layer.forward(x, ws=ws, y=y)
+    y2, idx, gate, counts = layer.forward(x, ws=ws, y=y, routing=True)
+    torch.cuda.synchronize()
+    counts_np = counts.cpu().numpy()
+
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.moe_profile_read()                      # clear
+    B.moe_profile_enable(True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        layer.forward(x, ws=ws, y=y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    B.moe_profile_enable(False)
+    stages = B.moe_profile_read()
+    ms_step = start.elapsed_time(end) / steps
+    log("bench: %.3f ms/step" % ms_step)
+    del layer, ws, x, y
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
+            "touched": int((counts_np > 0).sum())}
+
+
+def paired(args):
+    """Standard MoE against LatentMoE at the ablation shapes (equal d and m:
+    128 experts top-6 at d vs 512 experts top-22 at l = d/4), in prefill and in
+    batch decode.  One JSON line: per layer the step time, tokens/s, FLOP per
+    token, algorithmic bytes per token and the expert weight bytes a step
+    reads, and the latent/standard ratios."""
+    from sparse_moe_layer_fwd_amd.workloads import CONFIGS
+    out = {"metric": "standard vs latent MoE layer at the ablation shapes (paired, 1 MI355X)",
+           "unit": "ms per step", "steps": args.steps, "warmup": args.warmup,
+           "data": "synthetic (seeded random weights and inputs)", "pairs": []}
+    for regime, std_id, lat_id in (("prefill", 6, 3), ("decode", 7, 8)):
+        rec = {"regime": regime}
+        for role, cid in (("standard", std_id), ("latent", lat_id)):
+            cfg = CONFIGS[cid]
+            r = time_layer(cfg, cid, args.seed, args.steps, args.warmup)
+            rec[role] = {
+                "workload": cfg.name, "T": cfg.T, "d": cfg.d, "latent": cfg.latent,
+                "n_experts": cfg.n_experts, "top_k": cfg.top_k, "ffn": cfg.ffn,
+                "ms_per_step": round(r["ms_step"], 5),
+                "tokens_per_s": round(cfg.T / (r["ms_step"] * 1e-3), 1),
+                "flop_per_token": cfg.flops() / cfg.T,
+                "bytes_per_token": layer_bytes(cfg, r["touched"]) / cfg.T,
+                "expert_weight_gb_per_step": round(2 * r["touched"] * expert_weight_bytes_per_matrix(cfg) / 1e9, 4),
+                "experts_touched": r["touched"],
+                "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in r["stages"].items() if v[0]},
+            }
+        s_, l_ = rec["standard"], rec["latent"]
+        rec["latent_over_standard"] = {
+            "time": round(l_["ms_per_step"] / s_["ms_per_step"], 4),
+            "flop_per_token": round(l_["flop_per_token"] / s_["flop_per_token"], 4),
+            "bytes_per_token": round(l_["bytes_per_token"] / s_["bytes_per_token"], 4),
+            "expert_weight_bytes_per_step": round(l_["expert_weight_gb_per_step"] / s_["expert_weight_gb_per_step"], 4),
+        }
+        out["pairs"].append(rec)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +194,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paired", action="store_true",
+                    help="time the standard-vs-latent ablation pairs (configurations 6/3, 7/8) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
@@ -137,43 +223,15 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": max(1, args.steps)}))
         return
 
-    from sparse_moe_layer_fwd_amd import binding as B
-    from sparse_moe_layer_fwd_amd.layer import DeviceLayer, x_to_device
-    from sparse_moe_layer_fwd_amd.workloads import CONFIGS, Workload
+    from sparse_moe_layer_fwd_amd.workloads import CONFIGS
+
+    if args.paired:
+        paired(args)
+        return
 
     cfg = CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    log("bench: config %d %s, generating weights" % (args.config, cfg.name))
-    t0 = time.perf_counter()
-    wl = Workload(cfg, args.seed)
-    layer = DeviceLayer.from_workload(wl, device=dev, threads=16)
-    x = x_to_device(wl, dev)
-    y = torch.empty((cfg.T, cfg.d), dtype=layer.act_torch_dtype(), device=dev)
-    ws = layer.new_workspace(cfg.T)
-    torch.cuda.synchronize()
-    log("bench: inputs resident in HBM (%.1f s); warmup %d" % (time.perf_counter() - t0, args.warmup))
-
-    for _ in range(args.warmup):
-        layer.forward(x, ws=ws, y=y)
-    y2, idx, gate, counts = layer.forward(x, ws=ws, y=y, routing=True)
-    torch.cuda.synchronize()
-    counts_np = counts.cpu().numpy()
-    touched = int((counts_np > 0).sum())
-
-    stream = torch.cuda.current_stream(dev)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    B.moe_profile_read()                      # clear
-    B.moe_profile_enable(True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        layer.forward(x, ws=ws, y=y)
-    end.record(stream)
-    torch.cuda.synchronize()
-    B.moe_profile_enable(False)
-    stages = B.moe_profile_read()
-    ms_step = start.elapsed_time(end) / args.steps
-    log("bench: %.3f ms/step" % ms_step)
+    r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup)
+    ms_step, stages, counts_np, touched = r["ms_step"], r["stages"], r["counts"], r["touched"]
 
     # dominant kernel: the grouped expert GEMMs (two launches per step)
     n_up, ms_up = stages["expert_up"]

@@ -105,6 +105,18 @@ def _cfg_list():
         MoEConfig("latent_ultra_prefill_nvfp4", T=16384, d=8192, latent=2048,
                   n_experts=512, top_k=22, ffn=2048, expert="nvfp4", zipf_s=1.1,
                   description="LatentMoE Ultra-like prefill, NVFP4 experts, Zipf routing"),
+        # the ablation pair at equal d and m: standard MoE (128 experts, top-6 at
+        # d) against the latent layer of configuration 3 (512 experts, top-22 at
+        # l = d / 4), in prefill and in batch decode
+        MoEConfig("std_8b_prefill", T=8192, d=4096, latent=4096, n_experts=128, top_k=6,
+                  ffn=1024, has_latent_proj=False, zipf_s=1.1,
+                  description="Standard MoE at the ablation shape (paired with 3), Zipf routing"),
+        MoEConfig("std_8b_decode", T=64, d=4096, latent=4096, n_experts=128, top_k=6,
+                  ffn=1024, has_latent_proj=False,
+                  description="Standard MoE at the ablation shape, batch decode"),
+        MoEConfig("latent_8b_decode", T=64, d=4096, latent=1024, n_experts=512, top_k=22,
+                  ffn=1024,
+                  description="LatentMoE at the ablation shape (configuration 3), batch decode"),
     ]
 
 

@@ -1,4 +1,4 @@
-"""Parity at the full sizes of the five layer configurations, in the launch
+"""Parity at the full sizes of the layer configurations, in the launch
 configuration the benchmark times: routing (index sets, counts, gates) on every
 token, y on a seeded sample of tokens the oracle computes one by one."""
 import numpy as np
@@ -15,7 +15,7 @@ SAMPLE = 48
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5, 6, 7, 8])
 def test_full_size_config(cfg_id):
     cfg = CONFIGS[cfg_id]
     log("full config %d %s: preparing" % (cfg_id, cfg.name))
