@@ -7,6 +7,7 @@ GEMMs, combine and up-projection, all in libmoe.so on HBM-resident inputs.
 
     python bench.py [--config 3] [--steps 20] [--warmup 5] [--gpus 1]
     python bench.py --paired      # standard vs latent at the ablation shapes
+    python bench.py --paired router_at_d   # router on the latent vs on x at d
 
 Prints one JSON line.  `value` is tokens/s of the whole layer.  `roofline`
 describes the dominant kernel (the grouped expert GEMMs): its algorithmic
@@ -51,7 +52,7 @@ def layer_bytes(cfg, touched):
     b = 2 * touched * expert_weight_bytes_per_matrix(cfg)
     if cfg.has_latent_proj:
         b += 2 * cfg.d * cfg.latent * act
-    b += cfg.n_experts * cfg.latent * 4 + cfg.n_experts * 4
+    b += cfg.n_experts * (cfg.d if cfg.router_on_x else cfg.latent) * 4 + cfg.n_experts * 4
     b += 2 * cfg.n_shared * cfg.shared_ffn * cfg.d * act
     b += 2 * cfg.T * cfg.d * act
     return b
@@ -148,19 +149,31 @@ def time_layer(cfg, cfg_id, seed, steps, warmup):
             "touched": int((counts_np > 0).sum())}
 
 
+# Paired comparisons: (metric, (role a, role b), [(regime, config of a, config of b)])
+PAIRS = {
+    # standard MoE (128 experts top-6 at d) against LatentMoE (512 experts
+    # top-22 at l = d/4) at equal d and m
+    "ablation": ("standard vs latent MoE layer at the ablation shapes (paired, 1 MI355X)",
+                 ("standard", "latent"), [("prefill", 6, 3), ("decode", 7, 8)]),
+    # the latent layer with its router on the latent and no shared experts,
+    # against the same layer with the router and two shared experts at d
+    "router_at_d": ("LatentMoE with router on the latent vs router and shared experts at d "
+                    "(paired, 1 MI355X)", ("latent", "router_at_d"), [("prefill", 3, 9), ("decode", 8, 10)]),
+}
+
+
 def paired(args):
-    """Standard MoE against LatentMoE at the ablation shapes (equal d and m:
-    128 experts top-6 at d vs 512 experts top-22 at l = d/4), in prefill and in
-    batch decode.  One JSON line: per layer the step time, tokens/s, FLOP per
-    token, algorithmic bytes per token and the expert weight bytes a step
-    reads, and the latent/standard ratios."""
+    """Time the two layers of each pair back to back, in prefill and in batch
+    decode.  One JSON line: per layer the step time, tokens/s, FLOP per token,
+    algorithmic bytes per token and the expert weight bytes a step reads, and
+    the ratios of the second layer to the first."""
     from sparse_moe_layer_fwd_amd.workloads import CONFIGS
-    out = {"metric": "standard vs latent MoE layer at the ablation shapes (paired, 1 MI355X)",
-           "unit": "ms per step", "steps": args.steps, "warmup": args.warmup,
+    metric, (ra, rb), pairs = PAIRS[args.paired]
+    out = {"metric": metric, "unit": "ms per step", "steps": args.steps, "warmup": args.warmup,
            "data": "synthetic (seeded random weights and inputs)", "pairs": []}
-    for regime, std_id, lat_id in (("prefill", 6, 3), ("decode", 7, 8)):
+    for regime, a_id, b_id in pairs:
         rec = {"regime": regime}
-        for role, cid in (("standard", std_id), ("latent", lat_id)):
+        for role, cid in ((ra, a_id), (rb, b_id)):
             cfg = CONFIGS[cid]
             r = time_layer(cfg, cid, args.seed, args.steps, args.warmup)
             rec[role] = {
@@ -174,8 +187,8 @@ def paired(args):
                 "experts_touched": r["touched"],
                 "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in r["stages"].items() if v[0]},
             }
-        s_, l_ = rec["standard"], rec["latent"]
-        rec["latent_over_standard"] = {
+        s_, l_ = rec[ra], rec[rb]
+        rec["%s_over_%s" % (rb, ra)] = {
             "time": round(l_["ms_per_step"] / s_["ms_per_step"], 4),
             "flop_per_token": round(l_["flop_per_token"] / s_["flop_per_token"], 4),
             "bytes_per_token": round(l_["bytes_per_token"] / s_["bytes_per_token"], 4),
@@ -190,12 +203,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-5 (default 3)")
+    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-10 (default 3)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--paired", action="store_true",
-                    help="time the standard-vs-latent ablation pairs (configurations 6/3, 7/8) instead")
+    ap.add_argument("--paired", nargs="?", const="ablation", choices=sorted(PAIRS), default=None,
+                    help="time a pair of layers instead: 'ablation' (standard vs latent, "
+                         "configurations 6/3 and 7/8) or 'router_at_d' (3/9 and 8/10)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()

@@ -14,7 +14,9 @@
  *     one FP32 global scale (Korean summary, section 2.4 NVFP4 Training); the
  *     Ultra release ships NVFP4 routed experts (Ultra release news, quantization).
  * Readings taken where the pages are silent: the router is one linear layer
- * (fp32, optional bias) on the latent; gates are the softmax over the K selected
+ * (fp32, optional bias) on the latent, or on x at d when router_on_x is set (the
+ * Korean summary's LatentMoE section keeps routing and the shared experts at
+ * full width); gates are the softmax over the K selected
  * logits; the expert FFN is W2 * sqrelu(W1 * z) with sqrelu(h) = max(h,0)^2 and
  * no biases; equal logits select the lower expert id; routing is dropless.
  *
@@ -67,11 +69,15 @@ typedef struct {
   int32_t has_latent_proj; /* 1: LatentMoE; 0: standard MoE, latent == d    */
   int32_t act_dtype;       /* MOE_F32 or MOE_BF16: x, projections, y        */
   int32_t expert_dtype;    /* MOE_F32 (with act F32), MOE_BF16 or MOE_NVFP4 */
+  int32_t router_on_x;     /* 0: the router reads the latent z (W_r [N][l]);
+                              1: it reads x at d (W_r [N][d]), the router
+                              placement of the Korean Nemotron 3 summary,
+                              section 2.2 LatentMoE                           */
 } moe_config_t;
 
 typedef struct {
   const void* w_down;      /* [l][d] act dtype; NULL unless has_latent_proj          */
-  const float* w_router;   /* [N][l] fp32                                            */
+  const float* w_router;   /* [N][l] fp32 ([N][d] when router_on_x)                  */
   const float* b_router;   /* [N] fp32 added to the logits before top-K, or NULL     */
   const void* w1;          /* [N][m][l]; NVFP4: packed codes uint8 [N][m][l/2]       */
   const void* w2;          /* [N][l][m]; NVFP4: packed codes uint8 [N][l][m/2]       */

@@ -25,8 +25,8 @@ def margin_filter(wl, cfg, max_rounds=20):
     attempt = np.zeros(cfg.T, dtype=np.int64)
     bad = np.arange(cfg.T)
     for _ in range(max_rounds):
-        z = latent_down(decode_expert(x[bad], cfg.act), wd64)
-        lg = router_logits(z, wr, br)
+        xb = decode_expert(x[bad], cfg.act)
+        lg = router_logits(xb if cfg.router_on_x else latent_down(xb, wd64), wr, br)
         srt = -np.sort(-lg, axis=1)
         gap = srt[:, cfg.top_k - 1] - srt[:, cfg.top_k]
         bad = bad[gap < cfg.margin]

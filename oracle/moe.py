@@ -10,6 +10,7 @@ Method, per token (sources in ``oracle/__init__.py``):
   1. z = W_d x                (latent down-projection d -> l; [KO 2.2], [JA note])
      z = x                    (standard MoE: no projection, l = d)
   2. logits_e = W_r[e] . z + b_r[e]      (router GEMV on the latent; linear router)
+     logits_e = W_r[e] . x + b_r[e]      (router_on_x: routing at d as [KO 2.2] draws it)
   3. sel = the K experts of largest logit; ties go to the lower expert id
   4. g_k = softmax over the K selected logits
   5. u = sum_k g_k W2[sel_k] sqrelu(W1[sel_k] z),  sqrelu(h) = max(h, 0)^2
@@ -134,7 +135,8 @@ def latent_down(x64: np.ndarray, wd64: Optional[np.ndarray]) -> np.ndarray:
 
 
 def router_logits(z: np.ndarray, wr: np.ndarray, br: Optional[np.ndarray]) -> np.ndarray:
-    """logits[t][e] = sum_i W_r[e][i] z[t][i] + b_r[e] (linear router on the latent)."""
+    """logits[t][e] = sum_i W_r[e][i] z[t][i] + b_r[e]: a linear router on its
+    input z (the latent, or x at d when the layer routes on x)."""
     lg = z @ np.asarray(wr, dtype=np.float64).T
     if br is not None:
         lg = lg + np.asarray(br, dtype=np.float64)[None, :]
@@ -177,7 +179,9 @@ def route(layer, cfg) -> OracleResult:
     x64 = _act(layer.x(), cfg.act)
     wd = layer.w_down()
     z = latent_down(x64, None if wd is None else _act(wd, cfg.act))
-    logits = router_logits(z, layer.w_router(), layer.b_router())
+    # [KO 2.2] places the router at d (on x); the latent variant routes on z
+    logits = router_logits(x64 if cfg.router_on_x else z,
+                           layer.w_router(), layer.b_router())
     K = cfg.top_k
     idx = select_top_k(logits, K)
     gate = gates_softmax(logits, idx)
@@ -245,7 +249,7 @@ def forward_scalar(layer, cfg) -> OracleResult:
     ys, idxs, gates, lgs, zs = [], [], [], [], []
     for t in range(T):
         z = X[t] if Wd is None else matvec(Wd, X[t])
-        lg = [a + b for a, b in zip(matvec(Wr, z), Br)]
+        lg = [a + b for a, b in zip(matvec(Wr, X[t] if cfg.router_on_x else z), Br)]
         chosen = []
         for _ in range(K):                   # repeated selection of the best remaining
             best = None

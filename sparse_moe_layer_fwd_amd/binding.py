@@ -24,7 +24,7 @@ MOE_NUM_STAGES = 10
 class MoEConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d", "latent", "n_experts", "top_k", "ffn", "n_shared", "shared_ffn", "max_tokens",
-        "has_latent_proj", "act_dtype", "expert_dtype")]
+        "has_latent_proj", "act_dtype", "expert_dtype", "router_on_x")]
 
 
 class MoEWeights(ctypes.Structure):

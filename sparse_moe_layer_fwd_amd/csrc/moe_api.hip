@@ -248,6 +248,10 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
     a.C = at<void>(ws, p.z32); a.ldc = c.latent;
     if (p.f32) {
       MOE_TRY(dense_f32(a, false, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
+    } else if (c.router_on_x) {
+      // the router reads x, so only the experts' bf16 latent rows are needed
+      a.C = at<void>(ws, p.z16);
+      MOE_TRY(dense_bf16(a, EPI_BF16, h->num_cu, at<float>(ws, p.partial), s));
     } else {
       a.C2 = at<void>(ws, p.z16); a.ldc2 = c.latent;
       MOE_TRY(dense_bf16(a, EPI_Z, h->num_cu, at<float>(ws, p.partial), s));
@@ -256,13 +260,17 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
   {
     StageScope sc(MOE_STAGE_ROUTER, s);
     GemmArgs a = gemm_args();
-    a.A = c.has_latent_proj ? (const void*)at<float>(ws, p.z32) : x;
-    a.lda = c.latent;
-    a.B = w.w_router; a.ldb = c.latent;
-    a.M = T; a.N = c.n_experts; a.K = c.latent;
+    // the router's input: the fp32 latent z32, or x at d (also when there is
+    // no latent projection)
+    const bool on_x = c.router_on_x || !c.has_latent_proj;
+    const int kr = on_x ? c.d : c.latent;
+    a.A = on_x ? x : (const void*)at<float>(ws, p.z32);
+    a.lda = kr;
+    a.B = w.w_router; a.ldb = kr;
+    a.M = T; a.N = c.n_experts; a.K = kr;
     a.C = at<float>(ws, p.logits); a.ldc = c.n_experts;
     a.bias = w.b_router;
-    const bool a_bf16 = !c.has_latent_proj && c.act_dtype == MOE_BF16;
+    const bool a_bf16 = on_x && c.act_dtype == MOE_BF16;
     MOE_TRY(dense_f32(a, a_bf16, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
   }
   {
@@ -367,6 +375,7 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
   if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts) return MOE_ERR_INVALID_ARG;
   if (c.n_shared < 0 || (c.n_shared > 0 && c.shared_ffn <= 0)) return MOE_ERR_INVALID_ARG;
   if (c.has_latent_proj != 0 && c.has_latent_proj != 1) return MOE_ERR_INVALID_ARG;
+  if (c.router_on_x != 0 && c.router_on_x != 1) return MOE_ERR_INVALID_ARG;
   if (!c.has_latent_proj && c.latent != c.d) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c.max_tokens * c.top_k > (1 << 30)) return MOE_ERR_INVALID_ARG;
   if (c.act_dtype != MOE_F32 && c.act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;

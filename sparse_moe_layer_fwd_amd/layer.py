@@ -42,7 +42,8 @@ class DeviceLayer:
         c = B.MoEConfig(d=cfg.d, latent=cfg.latent, n_experts=cfg.n_experts, top_k=cfg.top_k,
                         ffn=cfg.ffn, n_shared=cfg.n_shared, shared_ffn=cfg.shared_ffn,
                         max_tokens=self.max_tokens, has_latent_proj=int(cfg.has_latent_proj),
-                        act_dtype=B.DTYPES[cfg.act], expert_dtype=B.DTYPES[cfg.expert])
+                        act_dtype=B.DTYPES[cfg.act], expert_dtype=B.DTYPES[cfg.expert],
+                        router_on_x=int(cfg.router_on_x))
         w = B.MoEWeights()
         for name in ("w_down", "w_router", "b_router", "w1", "w2", "w1_scale", "w2_scale",
                      "w1_gscale", "w2_gscale", "w_up", "ws1", "ws2"):

@@ -61,6 +61,7 @@ class MoEConfig:
     act: str = "bf16"      # "f32" | "bf16": x, projections, activations
     expert: str = "bf16"   # "f32" | "bf16" | "nvfp4": routed expert weights
     zipf_s: float = 0.0    # > 0: Zipf(s) expert-popularity bias in the router
+    router_on_x: bool = False  # router reads x at d instead of the latent z
     margin: float = 1e-4   # top-K gap required by the margin filter (tests)
     description: str = ""
 
@@ -70,7 +71,7 @@ class MoEConfig:
     # ---- algorithmic work (counts only what the method must compute/move) ----
     def flops(self) -> float:
         T, d, l, N, K, m = self.T, self.d, self.latent, self.n_experts, self.top_k, self.ffn
-        f = 2.0 * T * l * N                       # router
+        f = 2.0 * T * (d if self.router_on_x else l) * N   # router
         f += 4.0 * T * K * l * m                  # expert up + down
         if self.has_latent_proj:
             f += 4.0 * T * d * l                  # down + up projection
@@ -117,6 +118,15 @@ def _cfg_list():
         MoEConfig("latent_8b_decode", T=64, d=4096, latent=1024, n_experts=512, top_k=22,
                   ffn=1024,
                   description="LatentMoE at the ablation shape (configuration 3), batch decode"),
+        # configurations 3 and 8 with the router at d (on x) and two always-on
+        # shared experts at d beside the latent routed experts
+        MoEConfig("latent_8b_prefill_router_x", T=8192, d=4096, latent=1024, n_experts=512,
+                  top_k=22, ffn=1024, n_shared=2, shared_ffn=1024, router_on_x=True,
+                  zipf_s=1.1,
+                  description="LatentMoE, router and 2 shared experts at d, prefill, Zipf routing"),
+        MoEConfig("latent_8b_decode_router_x", T=64, d=4096, latent=1024, n_experts=512,
+                  top_k=22, ffn=1024, n_shared=2, shared_ffn=1024, router_on_x=True,
+                  description="LatentMoE, router and 2 shared experts at d, batch decode"),
     ]
 
 
@@ -227,7 +237,8 @@ class Workload:
 
     def w_router(self) -> np.ndarray:
         c = self.cfg
-        return self._normal("w_router", (c.n_experts, c.latent), 1.0 / math.sqrt(c.latent), 0)
+        fan_in = c.d if c.router_on_x else c.latent
+        return self._normal("w_router", (c.n_experts, fan_in), 1.0 / math.sqrt(fan_in), 0)
 
     def b_router(self) -> Optional[np.ndarray]:
         """Zipf(s) popularity bias: b_e = -s * ln(rank_e), rank a seeded permutation of 1..N."""

@@ -61,7 +61,8 @@ def f64_layer(cfg: MoEConfig, rng: np.random.Generator, T=None):
     x = rng.standard_normal((T, d))
     wd = rng.standard_normal((l, d)) / np.sqrt(d) if cfg.has_latent_proj else None
     wu = rng.standard_normal((d, l)) / np.sqrt(l) if cfg.has_latent_proj else None
-    wr = rng.standard_normal((N, l)) / np.sqrt(l)
+    kr = d if cfg.router_on_x else l
+    wr = rng.standard_normal((N, kr)) / np.sqrt(kr)
     w1 = rng.standard_normal((N, m, l)) / np.sqrt(l)
     w2 = rng.standard_normal((N, l, m)) / np.sqrt(m)
     ws1 = ws2 = None

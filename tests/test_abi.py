@@ -67,6 +67,7 @@ def _good_w(**kw):
     (dict(has_latent_proj=0), {}, B.MOE_ERR_INVALID_ARG),         # latent != d without projection
     (dict(act_dtype=7), {}, B.MOE_ERR_INVALID_ARG),
     (dict(n_shared=1, shared_ffn=0), {}, B.MOE_ERR_INVALID_ARG),
+    (dict(router_on_x=2), {}, B.MOE_ERR_INVALID_ARG),             # a flag: 0 or 1
     ({}, dict(w1=None), B.MOE_ERR_INVALID_ARG),
     ({}, dict(w_router=FAKE + 4), B.MOE_ERR_INVALID_ARG),        # misaligned
     ({}, dict(w_down=None), B.MOE_ERR_INVALID_ARG),

@@ -125,6 +125,15 @@ SMALL = {
                                 ffn=1024),
     "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
                                   top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
+    # routing on x at d (shared experts at d beside latent routed experts)
+    "router_on_x_shared": MoEConfig("router_on_x_shared", T=300, d=256, latent=128, n_experts=16,
+                                    top_k=4, ffn=128, n_shared=1, shared_ffn=128,
+                                    router_on_x=True),
+    "router_on_x_decode_nvfp4": MoEConfig("router_on_x_decode_nvfp4", T=40, d=512, latent=256,
+                                          n_experts=32, top_k=4, ffn=256, n_shared=1,
+                                          shared_ffn=256, expert="nvfp4", router_on_x=True),
+    "router_on_x_f32": MoEConfig("router_on_x_f32", T=120, d=128, latent=64, n_experts=8, top_k=2,
+                                 ffn=128, act="f32", expert="f32", margin=1e-3, router_on_x=True),
 }
 
 

@@ -309,6 +309,43 @@ def test_vectorised_matches_scalar_loops():
     assert np.allclose(a.y, b.y, rtol=1e-12, atol=1e-12)
 
 
+def test_router_on_x_equals_latent_router_through_inverse_projection():
+    """Routing on x with W_r equals routing on z = W_d x with W_r W_d^-1 (l = d,
+    W_d invertible and not symmetric): the router must read x, untransposed."""
+    rng = np.random.default_rng(21)
+    cfg = MoEConfig("rx", T=40, d=12, latent=12, n_experts=8, top_k=3, ffn=10, n_shared=1,
+                    shared_ffn=6, router_on_x=True)
+    c, layer = f64_layer(cfg, rng)
+    wd = layer.w_down() + 0.5 * np.eye(12)
+    assert not np.allclose(wd, wd.T)
+    layer._wd = wd
+    c_lat = c.replace(router_on_x=False)
+    lat = ArrayLayer(c_lat, layer.x(), layer.w_router() @ np.linalg.inv(wd), layer._w1,
+                     layer._w2, wd, layer.w_up(), None, layer._ws1, layer._ws2)
+    a = oracle.forward(layer, c)
+    b = oracle.forward(lat, c_lat)
+    assert np.allclose(a.logits, b.logits, rtol=1e-11, atol=1e-11)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.allclose(a.y, b.y, rtol=1e-11, atol=1e-11)
+    # and the same layer routed on z instead picks different experts
+    wrong = oracle.forward(ArrayLayer(c_lat, layer.x(), layer.w_router(), layer._w1, layer._w2,
+                                      wd, layer.w_up(), None, layer._ws1, layer._ws2), c_lat)
+    assert not np.array_equal(wrong.idx, a.idx)
+
+
+def test_router_on_x_vectorised_matches_scalar_loops():
+    rng = np.random.default_rng(22)
+    cfg = MoEConfig("rx", T=24, d=16, latent=8, n_experts=6, top_k=2, ffn=10, n_shared=1,
+                    shared_ffn=12, router_on_x=True)
+    c, layer = f64_layer(cfg, rng)
+    layer._br = rng.standard_normal(c.n_experts)
+    a = oracle.forward(layer, c)
+    b = oracle.forward_scalar(layer, c)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.allclose(a.gate, b.gate, rtol=1e-14, atol=1e-15)
+    assert np.allclose(a.y, b.y, rtol=1e-12, atol=1e-12)
+
+
 def test_token_subset_equals_full_rows():
     rng = np.random.default_rng(13)
     c, layer = f64_layer(SMALL, rng)
