@@ -28,9 +28,10 @@ if ROOT not in sys.path:
 
 METRIC = "LatentMoE layer tokens/sec on 1 MI355X; % MFMA peak (prefill), % HBM BW (decode)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (matrix)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-CPU_SAMPLE = {1: 64, 2: 1536, 3: 3072, 4: 64, 5: 384}
+CPU_SAMPLE = {1: 64, 2: 1536, 3: 3072, 4: 64, 5: 384, 11: 3072, 12: 64, 13: 384}
 
 
 def log(msg):
@@ -41,6 +42,8 @@ def expert_weight_bytes_per_matrix(cfg):
     el = cfg.latent * cfg.ffn
     if cfg.expert == "nvfp4":
         return el / 2 + el / 16 + 4
+    if cfg.expert == "fp8":
+        return el + 4
     return el * (4 if cfg.expert == "f32" else 2)
 
 
@@ -53,7 +56,7 @@ def layer_bytes(cfg, touched):
     if cfg.has_latent_proj:
         b += 2 * cfg.d * cfg.latent * act
     b += cfg.n_experts * (cfg.d if cfg.router_on_x else cfg.latent) * 4 + cfg.n_experts * 4
-    b += 2 * cfg.n_shared * cfg.shared_ffn * cfg.d * act
+    b += 2 * cfg.n_shared * cfg.shared_ffn * cfg.d * (1 if cfg.shared_fp8 else act)
     b += 2 * cfg.T * cfg.d * act
     return b
 
@@ -159,6 +162,10 @@ PAIRS = {
     # against the same layer with the router and two shared experts at d
     "router_at_d": ("LatentMoE with router on the latent vs router and shared experts at d "
                     "(paired, 1 MI355X)", ("latent", "router_at_d"), [("prefill", 3, 9), ("decode", 8, 10)]),
+    # the latent layers with bf16 experts against the same layers with FP8
+    # (E4M3) expert weights and activations
+    "fp8": ("LatentMoE with bf16 vs FP8 experts (paired, 1 MI355X)", ("bf16", "fp8"),
+            [("prefill", 3, 11), ("decode", 4, 12)]),
 }
 
 
@@ -203,13 +210,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-10 (default 3)")
+    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-13 (default 3)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paired", nargs="?", const="ablation", choices=sorted(PAIRS), default=None,
                     help="time a pair of layers instead: 'ablation' (standard vs latent, "
-                         "configurations 6/3 and 7/8) or 'router_at_d' (3/9 and 8/10)")
+                         "configurations 6/3 and 7/8), 'router_at_d' (3/9 and 8/10) or 'fp8' "
+                         "(bf16 vs FP8 experts, 3/11 and 4/12)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
@@ -257,7 +265,9 @@ def main():
     # intermediates of this implementation and are not counted
     flops_launch = 2.0 * cfg.T * cfg.top_k * cfg.latent * cfg.ffn
     bytes_launch = touched * expert_weight_bytes_per_matrix(cfg)
-    peak_f = PEAK_F32_TFLOPS if cfg.expert == "f32" else PEAK_BF16_TFLOPS
+    # the MFMA peak of the contraction's own dtype (NVFP4 weights are decoded
+    # to bf16 and run on the bf16 MFMA)
+    peak_f = {"f32": PEAK_F32_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.expert, PEAK_BF16_TFLOPS)
     t_mfma = flops_launch / (peak_f * 1e12)
     t_hbm = bytes_launch / (PEAK_HBM_GBS * 1e9)
     if t_hbm > t_mfma:
@@ -287,11 +297,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-weights/bf16" if cfg.expert == "nvfp4" else cfg.act,
+        "dtype": {"nvfp4": "nvfp4-weights/bf16", "fp8": "fp8-e4m3"}.get(cfg.expert, cfg.act),
         "data": "synthetic (seeded random weights and inputs, shapes of the layer configuration)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "latent": cfg.latent,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "ffn": cfg.ffn,
                    "n_shared": cfg.n_shared, "expert_dtype": cfg.expert,
+                   "shared_fp8": cfg.shared_fp8, "router_on_x": cfg.router_on_x,
                    "zipf_s": cfg.zipf_s, "experts_touched": touched,
                    "max_rows_per_expert": int(counts_np.max()), "parallelism": "single GPU"},
         "layer_tflops": round(cfg.flops() / (ms_step * 1e-3) / 1e12, 2),

@@ -13,6 +13,9 @@
  *   - NVFP4 expert weights: E2M1 elements, one E4M3 scale per 16-element block,
  *     one FP32 global scale (Korean summary, section 2.4 NVFP4 Training); the
  *     Ultra release ships NVFP4 routed experts (Ultra release news, quantization).
+ *   - FP8 (OCP E4M3) weights and activations: FP8 post-training quantisation of
+ *     weights and activations (Nemotron 3 Nano blog, FP8 quantisation section);
+ *     FP8 shared experts beside NVFP4 routed ones (Ultra release news).
  * Readings taken where the pages are silent: the router is one linear layer
  * (fp32, optional bias) on the latent, or on x at d when router_on_x is set (the
  * Korean summary's LatentMoE section keeps routing and the shared experts at
@@ -55,7 +58,7 @@ enum moe_status {
   MOE_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
 };
 
-enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2 };
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_NVFP4 = 2, MOE_FP8 = 3 };
 
 typedef struct {
   int32_t d;               /* hidden size                                   */
@@ -68,36 +71,59 @@ typedef struct {
   int32_t max_tokens;      /* largest T any call will pass                  */
   int32_t has_latent_proj; /* 1: LatentMoE; 0: standard MoE, latent == d    */
   int32_t act_dtype;       /* MOE_F32 or MOE_BF16: x, projections, y        */
-  int32_t expert_dtype;    /* MOE_F32 (with act F32), MOE_BF16 or MOE_NVFP4 */
+  int32_t expert_dtype;    /* MOE_F32 (with act F32), MOE_BF16, MOE_NVFP4 or
+                              MOE_FP8 (the last three with act BF16)          */
   int32_t router_on_x;     /* 0: the router reads the latent z (W_r [N][l]);
                               1: it reads x at d (W_r [N][d]), the router
                               placement of the Korean Nemotron 3 summary,
                               section 2.2 LatentMoE                           */
+  int32_t shared_fp8;      /* 0: shared expert weights in the act dtype;
+                              1: FP8 E4M3 (act BF16, n_shared > 0)            */
 } moe_config_t;
 
 typedef struct {
   const void* w_down;      /* [l][d] act dtype; NULL unless has_latent_proj          */
   const float* w_router;   /* [N][l] fp32 ([N][d] when router_on_x)                  */
   const float* b_router;   /* [N] fp32 added to the logits before top-K, or NULL     */
-  const void* w1;          /* [N][m][l]; NVFP4: packed codes uint8 [N][m][l/2]       */
-  const void* w2;          /* [N][l][m]; NVFP4: packed codes uint8 [N][l][m/2]       */
+  const void* w1;          /* [N][m][l]; NVFP4: packed codes uint8 [N][m][l/2];
+                              FP8: E4M3 codes uint8 [N][m][l]                  */
+  const void* w2;          /* [N][l][m]; NVFP4: packed codes uint8 [N][l][m/2];
+                              FP8: E4M3 codes uint8 [N][l][m]                  */
   const uint8_t* w1_scale; /* NVFP4 only: E4M3 bytes [N][m][l/16], else NULL          */
   const uint8_t* w2_scale; /* NVFP4 only: E4M3 bytes [N][l][m/16], else NULL          */
-  const float* w1_gscale;  /* NVFP4 only: [N] fp32 global scales, else NULL           */
-  const float* w2_gscale;  /* NVFP4 only: [N] fp32 global scales, else NULL           */
+  const float* w1_gscale;  /* NVFP4: [N] fp32 global scales; FP8: [N] fp32 per-matrix
+                              weight scales; else NULL                          */
+  const float* w2_gscale;  /* as w1_gscale, for W2                                  */
   const void* w_up;        /* [d][l] act dtype; NULL unless has_latent_proj          */
-  const void* ws1;         /* [S][shared_ffn][d] act dtype, NULL if S == 0           */
-  const void* ws2;         /* [S][d][shared_ffn] act dtype, NULL if S == 0           */
+  const void* ws1;         /* [S][shared_ffn][d] act dtype (E4M3 codes if shared_fp8),
+                              NULL if S == 0                                    */
+  const void* ws2;         /* [S][d][shared_ffn] act dtype (E4M3 codes if shared_fp8),
+                              NULL if S == 0                                    */
+  const float* act_scale;  /* FP8 experts: [2] fp32, the per-tensor scales of the
+                              expert inputs z (W1's) and h (W2's); else NULL   */
+  const float* ws1_scale;  /* shared_fp8: [1] fp32 weight scale of all of ws1     */
+  const float* ws2_scale;  /* shared_fp8: [1] fp32 weight scale of all of ws2     */
+  const float* shared_act_scale; /* shared_fp8: [2] fp32 per-tensor scales of x and
+                              of the shared hidden activations; else NULL     */
 } moe_weights_t;
 /* NVFP4 packing: element 2j of a row in the low nibble of byte j, element 2j+1
  * in the high nibble; block b of a row covers elements 16b..16b+15 along the
- * reduction dimension; w = e2m1(code) * e4m3(scale) * gscale[expert]. */
+ * reduction dimension; w = e2m1(code) * e4m3(scale) * gscale[expert].
+ * FP8 (OCP E4M3: bias 7, no infinities, 448 the largest finite value, S.1111.111
+ * NaN): a weight is e4m3(code) * its matrix scale.  An FP8 GEMM input v with
+ * per-tensor scale a is quantised as code = RNE_e4m3(clamp(fp32(v) * r, -448,
+ * 448)), r = 1/a as a correctly rounded fp32, and stands for a * e4m3(code).
+ * The S shared experts form one FFN of width S * shared_ffn, hence one scale
+ * per shared weight tensor.  Scale pointers are device pointers, 4-byte aligned. */
 
 /* Create a handle for one layer.  Host only: validates the configuration and
  * weight pointers, binds the caller-owned weights, reads the current device's
  * compute-unit count.  No device work.
  * Shape rules: d, l, m, shared_ffn multiples of 64; N <= 1024; K <= min(N, 64);
- * act F32 requires expert F32; act BF16 requires expert BF16 or NVFP4.
+ * act F32 requires expert F32; act BF16 requires expert BF16, NVFP4 or FP8.
+ * FP8 experts: l and m multiples of 128 and at least 256.  shared_fp8: d and
+ * shared_ffn multiples of 128, d and n_shared * shared_ffn at least 256.
+ * Outside these rules the call returns MOE_ERR_UNSUPPORTED.
  * Returns MOE_ERR_NO_DEVICE when no HIP device is visible. */
 int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out);
 
@@ -119,6 +145,12 @@ int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gat
 int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
                 int32_t* counts, void* ws, size_t ws_bytes, void* stream);
 
+/* Quantise n bf16 values (device, 16-byte aligned) to OCP FP8 E4M3 codes
+ * (device, 16-byte aligned) with the per-tensor scale *scale (device fp32):
+ * the FP8 input rule above.  For callers preparing FP8 weights or activations.
+ * n must be a multiple of 16; n == 0 enqueues nothing.  Enqueued on `stream`. */
+int moe_quantize_fp8(const void* in, int64_t n, const float* scale, uint8_t* out, void* stream);
+
 /* Release a handle (host memory only).  NULL is accepted. */
 int moe_destroy(moe_handle_t h);
 
@@ -126,12 +158,15 @@ int moe_destroy(moe_handle_t h);
 const char* moe_status_string(int status);
 
 /* ---- stage timing (benchmarks; off by default) ----
- * Stages of one call, in launch order.  EXPERT_UP and EXPERT_DOWN are the two
- * grouped expert GEMMs; SHARED covers both shared-expert GEMMs. */
+ * Stages of one call, in launch order (QUANT, numbered last, runs before
+ * EXPERT_UP).  EXPERT_UP and EXPERT_DOWN are the two
+ * grouped expert GEMMs; SHARED covers both shared-expert GEMMs (and the FP8
+ * quantisation of their input); QUANT is the FP8 quantisation of x for FP8
+ * routed experts of a layer without latent projection. */
 enum moe_stage {
   MOE_STAGE_DOWN_PROJ = 0, MOE_STAGE_ROUTER, MOE_STAGE_TOPK, MOE_STAGE_SCAN,
   MOE_STAGE_SCATTER, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_SHARED,
-  MOE_STAGE_COMBINE, MOE_STAGE_UP_PROJ, MOE_NUM_STAGES
+  MOE_STAGE_COMBINE, MOE_STAGE_UP_PROJ, MOE_STAGE_QUANT, MOE_NUM_STAGES
 };
 
 /* enable = 1: later moe_route / moe_forward calls record a HIP event pair

@@ -14,13 +14,13 @@ Nemotron 3 white paper and reports):
   [JA note]  "Nemotron 3: Efficient and Open Intelligence" wiki note
              (notes.yuuk.io), 提案手法 2 "LatentMoE".
   [Nano]     "Nemotron 3 Nano" blog post (jiwasawa.github.io), section on the
-             granular Mixture-of-Experts.
+             granular Mixture-of-Experts, and its FP8 quantisation section.
   [Ultra]    "NVIDIA AI、Nemotron 3 Ultraをリリース" (news.chathome.org),
              architecture and quantization paragraphs.
 Parity status of each function is stated in its docstring.
 """
 from .moe import (  # noqa: F401
     E2M1_TABLE, E4M3_TABLE, OracleResult, bf16_to_f64, decode_expert, decode_nvfp4,
-    e2m1_value, e4m3_value, expert_ffn, forward, forward_scalar, gates_softmax,
+    e2m1_value, e4m3_qdq, e4m3_quantize, e4m3_value, expert_ffn, forward, forward_scalar, gates_softmax,
     latent_down, router_logits, route, select_top_k, sqrelu,
 )

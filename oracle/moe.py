@@ -18,6 +18,11 @@ Method, per token (sources in ``oracle/__init__.py``):
   6. y = W_u u                (latent up-projection l -> d; [KO 2.2])
   7. y += sum_s Ws2[s] sqrelu(Ws1[s] x)  (always-on shared experts at d; [Nano],
      kept outside the latent compression per [KO 2.2])
+FP8 layers ([Nano] FP8 post-training quantisation of weights and activations;
+[Ultra] FP8 shared experts): weights are E4M3 codes times a per-matrix scale;
+every GEMM input is replaced by q(v) = a * e4m3(Q(v, a)) with its static
+per-tensor scale a (z or x before the first expert GEMM, the squared-ReLU
+hidden rows before the second), Q as in ``e4m3_quantize``.
 Readings where the pages are silent (router on the latent, softmax over the
 selected K, squared-ReLU, no biases in the FFN, tie rule, Zipf bias added to the
 logits) are listed with reasons in the repository's design notes.
@@ -80,6 +85,40 @@ E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 E4M3_TABLE = np.array([e4m3_value(b) for b in range(256)], dtype=np.float64)
 
 
+def e4m3_quantize(v, scale) -> np.ndarray:
+    """E4M3 codes of v / scale: the FP8 activation rule of the layer.
+
+    The decision is taken in fp32, the precision of the kernels' accumulators:
+    t = fp32(fp32(v) * r) with r = 1 / scale correctly rounded to fp32; t is
+    clamped to [-448, 448] (E4M3 has no infinities; 448 is its largest finite
+    value) and rounded to the nearest E4M3 value, ties to the even mantissa.
+    The sign bit is t's (a negative t that rounds to 0 gives code 0x80).
+    Pinned: torch.float8_e4m3fn's rounding on in-range values, hand-worked
+    ties, saturation, and code -> value -> code round trips.
+    """
+    r = np.float32(1.0) / np.float32(scale)
+    t = np.asarray(v, dtype=np.float32) * r                    # fp32 product (IEEE, RNE)
+    t = np.clip(t, np.float32(-448.0), np.float32(448.0)).astype(np.float64)
+    sign = np.signbit(t).astype(np.uint8) << 7
+    a = np.abs(t)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6                                        # below the smallest normal
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)    # multiples of 2^-9; 8 -> 0x08
+    nrm = ~sub
+    mant, ex = np.frexp(a[nrm])                                # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1
+    q = np.rint((mant * 2.0 - 1.0) * 8.0).astype(np.int64)     # 3 mantissa bits, ties to even
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    code[nrm] = ((e + 7) << 3) | q
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_qdq(v, scale) -> np.ndarray:
+    """The value an FP8 GEMM input v stands for: scale * e4m3(Q(v, scale))."""
+    return E4M3_TABLE[e4m3_quantize(v, scale)] * float(np.float32(scale))
+
+
 def decode_nvfp4(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
     """Two-level NVFP4 decode: w[r][c] = e2m1(code[r][c]) * e4m3(scale[r][c//16]) * g.
 
@@ -107,6 +146,9 @@ def decode_expert(stored, dtype: str) -> np.ndarray:
     if dtype == "nvfp4":
         codes, scales, g = stored
         return decode_nvfp4(codes, scales, g)
+    if dtype == "fp8":                      # (E4M3 codes, per-matrix fp32 scale)
+        codes, sc = stored
+        return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)] * float(np.float32(sc))
     if dtype == "bf16":
         return bf16_to_f64(stored)
     if dtype == "f32":
@@ -157,9 +199,13 @@ def gates_softmax(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return w / w.sum(axis=1, keepdims=True)
 
 
-def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """W2 sqrelu(W1 z) for each row z (W1 [m][l], W2 [l][m], float64)."""
-    return sqrelu(z_rows @ w1.T) @ w2.T
+def expert_ffn(z_rows: np.ndarray, w1: np.ndarray, w2: np.ndarray, h_scale=None) -> np.ndarray:
+    """W2 sqrelu(W1 z) for each row z (W1 [m][l], W2 [l][m], float64).  With
+    h_scale (FP8 layers) the hidden rows enter W2 as their FP8 values q(h)."""
+    h = sqrelu(z_rows @ w1.T)
+    if h_scale is not None:
+        h = e4m3_qdq(h, h_scale)
+    return h @ w2.T
 
 
 @dataclasses.dataclass
@@ -207,20 +253,29 @@ def forward(layer, cfg, tokens: Optional[Sequence[int]] = None) -> OracleResult:
     u = np.zeros((len(tok), cfg.latent), dtype=np.float64)
     idx_sub = r.idx[tok]
     gate_sub = r.gate[tok]
+    zin, h_scale = r.z[tok], None
+    if cfg.expert == "fp8":                          # FP8 expert inputs
+        a_z, h_scale = layer.act_scales()
+        zin = e4m3_qdq(zin, a_z)
     for e in np.unique(idx_sub):
         rows, ks = np.nonzero(idx_sub == e)          # each token picks e at most once
         w1 = decode_expert(layer.w1(int(e)), cfg.expert)
         w2 = decode_expert(layer.w2(int(e)), cfg.expert)
-        out = expert_ffn(r.z[tok[rows]], w1, w2)
+        out = expert_ffn(zin[rows], w1, w2, h_scale)
         u[rows] += gate_sub[rows, ks][:, None] * out
     wu = layer.w_up()
     y = u if wu is None else u @ _act(wu, cfg.act).T
     if cfg.n_shared:
         x64 = _act(layer.x(), cfg.act)[tok]
-        ws1 = _act(layer.ws1(), cfg.act)
-        ws2 = _act(layer.ws2(), cfg.act)
+        sdt = "fp8" if cfg.shared_fp8 else cfg.act
+        ws1 = decode_expert(layer.ws1(), sdt)
+        ws2 = decode_expert(layer.ws2(), sdt)
+        hs_scale = None
+        if cfg.shared_fp8:
+            a_x, hs_scale = layer.shared_act_scales()
+            x64 = e4m3_qdq(x64, a_x)
         for s in range(cfg.n_shared):
-            y = y + expert_ffn(x64, ws1[s], ws2[s])
+            y = y + expert_ffn(x64, ws1[s], ws2[s], hs_scale)
     r.y = y
     r.tokens = tok
     return r
@@ -242,6 +297,11 @@ def forward_scalar(layer, cfg) -> OracleResult:
     W1 = [decode_expert(layer.w1(e), cfg.expert).tolist() for e in range(cfg.n_experts)]
     W2 = [decode_expert(layer.w2(e), cfg.expert).tolist() for e in range(cfg.n_experts)]
     T, K, N, L, M = len(X), cfg.top_k, cfg.n_experts, cfg.latent, cfg.ffn
+    fp8 = cfg.expert == "fp8"
+    a_z, a_h = layer.act_scales() if fp8 else (None, None)
+
+    def q(vec, a):                           # an FP8 GEMM input's value (identity if a is None)
+        return vec if a is None else [float(v) for v in e4m3_qdq(np.array(vec), a)]
 
     def matvec(W, v):
         return [math.fsum(wi * vi for wi, vi in zip(row, v)) for row in W]
@@ -264,16 +324,20 @@ def forward_scalar(layer, cfg) -> OracleResult:
         s = math.fsum(ex)
         g = [v / s for v in ex]
         u = [0.0] * L
+        zq = q(z, a_z)
         for k, e in enumerate(chosen):
-            h = [max(v, 0.0) ** 2 for v in matvec(W1[e], z)]
+            h = q([max(v, 0.0) ** 2 for v in matvec(W1[e], zq)], a_h)
             o = matvec(W2[e], h)
             u = [ui + g[k] * oi for ui, oi in zip(u, o)]
         y = u if Wu is None else matvec(Wu, u)
         if cfg.n_shared:
-            S1 = _act(layer.ws1(), cfg.act).tolist()
-            S2 = _act(layer.ws2(), cfg.act).tolist()
+            sdt = "fp8" if cfg.shared_fp8 else cfg.act
+            S1 = decode_expert(layer.ws1(), sdt).tolist()
+            S2 = decode_expert(layer.ws2(), sdt).tolist()
+            a_x, a_s = layer.shared_act_scales() if cfg.shared_fp8 else (None, None)
+            xq = q(X[t], a_x)
             for sidx in range(cfg.n_shared):
-                h = [max(v, 0.0) ** 2 for v in matvec(S1[sidx], X[t])]
+                h = q([max(v, 0.0) ** 2 for v in matvec(S1[sidx], xq)], a_s)
                 o = matvec(S2[sidx], h)
                 y = [a + b for a, b in zip(y, o)]
         ys.append(y)

@@ -1,4 +1,4 @@
-"""ctypes binding of libmoe.so: the same six entry points as include/moe.h.
+"""ctypes binding of libmoe.so: the entry points of include/moe.h, same names.
 
 Argument marshalling only; every step of the layer runs in the HIP library.
 Importing this module does not load the library; ``lib()`` does, and raises
@@ -13,24 +13,26 @@ from .build import LIB_PATH
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_DEVICE, \
     MOE_ERR_HIP = range(6)
-MOE_F32, MOE_BF16, MOE_NVFP4 = 0, 1, 2
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4}
+MOE_F32, MOE_BF16, MOE_NVFP4, MOE_FP8 = 0, 1, 2, 3
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "fp8": MOE_FP8}
 
-EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_destroy",
-            "moe_status_string", "moe_profile_enable", "moe_profile_read", "moe_stage_name")
-MOE_NUM_STAGES = 10
+EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_quantize_fp8",
+            "moe_destroy", "moe_status_string", "moe_profile_enable", "moe_profile_read",
+            "moe_stage_name")
+MOE_NUM_STAGES = 11
 
 
 class MoEConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d", "latent", "n_experts", "top_k", "ffn", "n_shared", "shared_ffn", "max_tokens",
-        "has_latent_proj", "act_dtype", "expert_dtype", "router_on_x")]
+        "has_latent_proj", "act_dtype", "expert_dtype", "router_on_x", "shared_fp8")]
 
 
 class MoEWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_down", "w_router", "b_router", "w1", "w2", "w1_scale", "w2_scale", "w1_gscale",
-        "w2_gscale", "w_up", "ws1", "ws2")]
+        "w2_gscale", "w_up", "ws1", "ws2", "act_scale", "ws1_scale", "ws2_scale",
+        "shared_act_scale")]
 
 
 class MoEError(RuntimeError):
@@ -60,6 +62,8 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.moe_route.restype = ctypes.c_int
     L.moe_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_quantize_fp8.argtypes = [vp, ctypes.c_int64, vp, vp, vp]
+    L.moe_quantize_fp8.restype = ctypes.c_int
     L.moe_destroy.argtypes = [vp]
     L.moe_destroy.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -111,6 +115,13 @@ def moe_forward(h, x, T, y, idx, gate, counts, ws, ws_bytes, stream, check: bool
     st = lib().moe_forward(h, x, int(T), y, idx, gate, counts, ws, int(ws_bytes), stream)
     if check:
         _check(st, "moe_forward")
+    return st
+
+
+def moe_quantize_fp8(x, n, scale, out, stream, check: bool = True) -> int:
+    st = lib().moe_quantize_fp8(x, int(n), scale, out, stream)
+    if check:
+        _check(st, "moe_quantize_fp8")
     return st
 
 

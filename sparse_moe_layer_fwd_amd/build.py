@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
-SOURCES = ["moe_api.hip", "route.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_skinny.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_skinny.hip", "quant.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 ALU ops stay off: the compiler must not form v_pk_* fp32 math.

@@ -37,7 +37,35 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
+// OCP FP8 E4M3 quantisation: code = RNE_e4m3(clamp(v * r, -448, 448)), r the
+// fp32 reciprocal of the per-tensor scale.  The hardware conversion rounds to
+// nearest even; the clamp makes the saturation explicit (the format has no
+// infinities and 448 is its largest finite value).
+__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+// four values -> four codes in one dword (first value in the low byte)
+__device__ __forceinline__ uint32_t q8x4(float a, float b, float c, float d, float r) {
+  int q = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a * r), sat448(b * r), 0, false);
+  q = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c * r), sat448(d * r), q, true);
+  return (uint32_t)q;
+}
+__device__ __forceinline__ uint32_t q8(float v, float r) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(v * r), 0.0f, 0, false) & 0xFFu;
+}
+// E4M3 -> bf16, exact (every E4M3 value is a bf16 value): codes 2w, 2w+1 of
+// the 16-bit word `HI` of w -> bf16x2 (lower code in the low half)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// 8 codes (two dwords) -> 8 bf16 (one uint4)
+__device__ __forceinline__ uint4 e4m3x8_bf(uint32_t lo, uint32_t hi) {
+  return make_uint4(e4m3x2_bf<false>(lo), e4m3x2_bf<true>(lo), e4m3x2_bf<false>(hi), e4m3x2_bf<true>(hi));
+}
+
 // ------------------------------------------------------------------ kernel params
+// Weight (B operand) storage of a GEMM.  FP8: A and B are both E4M3 codes.
+enum WType : int { WT_BF16 = 0, WT_NVFP4 = 1, WT_FP8 = 2 };
+
 enum Epi : int {
   EPI_BF16 = 0,        // C(bf16) = g*acc                             (expert down, dense)
   EPI_Z = 1,           // C(f32) = acc and C2(bf16) = acc             (latent z32 / z16)
@@ -46,11 +74,16 @@ enum Epi : int {
   EPI_BF16_ADD = 5,    // C(bf16) = acc + add[r][c] (fp32)            (up-proj + shared)
   EPI_SQRELU_F32 = 6,  // C(f32) = max(acc,0)^2
   EPI_F32_ADD = 8,     // C(f32) = acc + add[r][c]
-  EPI_PARTIAL = 9      // C(f32)[slice blockIdx.y] = acc over that slice of K (split-K)
+  EPI_PARTIAL = 9,     // C(f32)[slice blockIdx.y] = acc over that slice of K (split-K)
+  EPI_Z8 = 10,         // C(f32) = acc and C2(e4m3) = q(acc)          (latent z32 / z8)
+  EPI_Q8 = 11,         // C(e4m3) = q(acc)                            (latent z8 only)
+  EPI_SQRELU_Q8 = 12   // C(e4m3) = q(max(g*acc,0)^2)                 (FP8 expert up)
 };
-// g: the NVFP4 per-expert global scale (1 for bf16 weights).  Gates are not
-// applied by any GEMM: the combine step multiplies each expert output by its
-// gate while summing a token's K outputs.
+// g: the weight scale times the activation scale: the NVFP4 per-expert global
+// scale or the FP8 per-matrix weight scale (b_gscale[group]), times the FP8
+// per-tensor scale of the A operand (*a_scale); 1 where absent.  q(v): E4M3
+// code of v / *q_scale.  Gates are not applied by any GEMM: the combine step
+// multiplies each expert output by its gate while summing a token's K outputs.
 
 // A tile row source.  Logical row r of the GEMM reads physical row
 // a_rows ? a_rows[r] : r of A.
@@ -59,7 +92,9 @@ struct GemmArgs {
   const void* B; int64_t ldb; int64_t b_gstride;     // element units (bf16/f32) or bytes (fp4 codes)
   int32_t kseg; int64_t b_segstride;                  // k split into segments of kseg (shared W2)
   const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;  // NVFP4 scales
-  const float* b_gscale;                              // NVFP4 per-group global scale
+  const float* b_gscale;                              // NVFP4 / FP8 per-group weight scale
+  const float* a_scale;                               // FP8 A: per-tensor scale (device scalar)
+  const float* q_scale;                               // FP8 outputs: per-tensor scale
   int32_t M, N, K;
   const int4* tiles; const int* n_tiles;              // grouped: (group, row0, row1, -)
   const int4* tiles2;                                 // grouped: second (remainder) list
@@ -69,14 +104,15 @@ struct GemmArgs {
 };
 
 struct SkinnyArgs {
-  const uint16_t* A; int64_t lda; const int* a_rows;
+  const void* A; int64_t lda; const int* a_rows;      // bf16, or E4M3 codes with FP8 weights
   const void* B; int64_t ldb; int64_t b_gstride;
   const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;
   const float* b_gscale;
+  const float* a_scale; const float* q_scale;
   int32_t N, K;
   const int* counts; const int* offs;
   int32_t max_rows;                                   // experts with >= max_rows rows are skipped
-  uint16_t* C; int64_t ldc;
+  void* C; int64_t ldc;
   float* P; int64_t p_slice;                          // split-K partials: slice s at P + s * p_slice
 };
 
@@ -88,15 +124,21 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_
 // Every dimension of the fp32 kernel: K % (32 * ks) == 0.
 hipError_t launch_gemm_f32_splitk(const GemmArgs& a, bool a_is_bf16, int epi, int ks, float* P,
                                   hipStream_t s);
-// bf16 dense GEMM with M <= 64 on the skinny kernel, K split into ks slices
-// (K % (256 * ks) == 0, N % 64 == 0), then the same sum and epilogue.
-hipError_t launch_skinny_splitk(const GemmArgs& a, int epi, int ks, float* P, hipStream_t s);
+// bf16 or FP8 (fp8: A and B E4M3 codes) dense GEMM with M <= 64 on the
+// skinny kernel, K split into ks slices (K % (256 * ks) == 0, N % 64 == 0),
+// then the same sum and epilogue.
+hipError_t launch_skinny_splitk(const GemmArgs& a, bool fp8, int epi, int ks, float* P, hipStream_t s);
 // out = epi( sum over the ks slices of P ), one thread per output element
 hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float* P, hipStream_t s);
 // num_cu: compute units of the device (the persistent grid is sized from it)
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
+// wt: WT_BF16, WT_NVFP4 (B only) or WT_FP8 (A and B; every size, stride and
+// leading dimension in elements = bytes, all even)
+hipError_t launch_gemm_bf16(const GemmArgs& a, int wt, int epi, int bm, int bn, int bms,
                             int64_t max_items, int num_cu, hipStream_t s);
-hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s);
+hipError_t launch_skinny(const SkinnyArgs& a, int wt, int epi, int n_experts, hipStream_t s);
+// out[i] = E4M3 code of in[i] / *scale (in bf16), n % 16 == 0
+hipError_t launch_quant_fp8(const uint16_t* in, int64_t n, const float* scale, uint8_t* out,
+                            hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,

@@ -11,7 +11,16 @@
 // section 2.4 NVFP4 Training) are staged raw in LDS and decoded exactly to bf16
 // in registers by each wavefront right before its MFMAs (every e2m1*e4m3
 // product is a bf16 value); the global scale multiplies the fp32 accumulator in
-// the epilogue.
+// the epilogue.  Or both operands are FP8 E4M3 codes (FP8 post-training
+// quantisation of weights and activations, Nemotron 3 Nano blog, FP8
+// quantisation section; FP8 shared experts, Ultra release news): the loads and
+// LDS layout are those of a bf16 GEMM over K/2 (two codes per 16-bit slot),
+// two 16-wide bf16 substeps form one 64-deep step of
+// v_mfma_f32_32x32x64_f8f6f4 (each lane's 32 bytes: its 16 bytes of both
+// substeps; A and B take the same k for each lane and byte, so the dot
+// product is unchanged), and the per-tensor scales multiply the accumulator.
+// FP8 outputs (the activations of the next FP8 GEMM) are quantised in the
+// epilogue.
 //
 // Data movement: operands go global -> LDS with gfx950's direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
@@ -83,7 +92,6 @@ __device__ __forceinline__ Fp4Scale split_scale(uint32_t e4m3) {
 }
 template <int BYTE>
 __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, const Fp4Scale& sc) {
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
   const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.pow2, BYTE));
   const float lo = __uint_as_float(pr << 16) * sc.frac;
   const float hi = __uint_as_float(pr & 0xFFFF0000u) * sc.frac;
@@ -96,9 +104,9 @@ __device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
 
 }  // namespace
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
 struct TileCfg {
-  static constexpr bool IS_FP4 = FP4;
+  static constexpr bool FP4 = WT == WT_NVFP4, IS_FP4 = FP4, IS_FP8 = WT == WT_FP8;
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per bf16 row
   static constexpr int A_BYTES = BM * BK * 2;
@@ -121,10 +129,9 @@ struct TileCfg {
   static constexpr int TM = WM / 32, TN = WN / 32;             // 32x32 MFMA blocks per wavefront
   static_assert(A_TOT >= 1 && B_TOT >= 1 && (!FP4 || S_TOT >= 1), "tile too small");
   static_assert(LOADS * (NST - 1) < 64, "vmcnt range");
-  // staged bf16 epilogue: 16-byte stores per thread and tile (all issued)
-  static constexpr int EPI_STORES = TM * (32 * WGM * (BN / 8)) / NT;
   static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
+  static_assert(!IS_FP8 || BK % 32 == 0, "FP8: whole 64-code steps per k-tile");
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -203,10 +210,11 @@ __device__ __forceinline__ void item_coords(const GemmArgs& p, const int4* list,
   n0 = nt * BN;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
 __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r1, int n0,
-                                         TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& s) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+                                         TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& s) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  constexpr bool FP4 = C::FP4;
   constexpr int CPR = C::CPR, NW = C::NW;
   constexpr int RPB = 64 / CPR;                    // A rows per 1 KB DMA block
   const int lane = threadIdx.x & 63;
@@ -271,11 +279,12 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
 }
 
 // Direct-to-LDS loads of k-tile kt of a tile into one stage.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
 __device__ __forceinline__ void issue_tile(const GemmArgs& p,
-                                           const TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& s,
+                                           const TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& s,
                                            int kt, char* stage) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  constexpr bool FP4 = C::FP4;
   constexpr int NW = C::NW;
   const int wave = threadIdx.x >> 6;
   const uint32_t k0 = (uint32_t)kt * BK;
@@ -311,51 +320,67 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
 
 // Epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
 // col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
-// bf16 outputs go through LDS (`stage`, EPB bytes): a lane's own values cover
-// 16 bytes of each of 32 rows per store, so they are transposed one i-block
-// (32 rows per wavefront row) at a time and written back as whole 16-byte
-// units, each wavefront store covering complete rows of the tile.  Contains
-// barriers: every wavefront of the block calls it.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+// bf16 and E4M3 outputs go through LDS (`stage`, EPB bytes): a lane's own
+// values cover 8 (bf16) or 4 (E4M3) bytes of each of 32 rows per store, so they
+// are transposed one i-block (32 rows per wavefront row) at a time and written
+// back as whole 16-byte units, each wavefront store covering complete rows of
+// the tile.  Contains barriers: every wavefront of the block calls it.
+template <int EPI>
+struct EpiKind {
+  static constexpr bool STAGED = EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16 || EPI == EPI_Q8 ||
+                                 EPI == EPI_SQRELU_Q8;
+  static constexpr int ELEM = (EPI == EPI_Q8 || EPI == EPI_SQRELU_Q8) ? 1 : 2;   // staged output bytes
+  static constexpr bool SQRELU = EPI == EPI_SQRELU_BF16 || EPI == EPI_SQRELU_Q8;
+  static constexpr bool Q8 = EPI == EPI_Q8 || EPI == EPI_SQRELU_Q8 || EPI == EPI_Z8;
+};
+
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
 __device__ __forceinline__ void epilogue_tile(
     const GemmArgs& p, int g, int r0, int r1, int n0, char* stage,
-    f32x16 (&acc)[TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TN][TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>::TM]) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+    f32x16 (&acc)[TileCfg<BM, BN, BK, WGM, WGN, NST, WT>::TN][TileCfg<BM, BN, BK, WGM, WGN, NST, WT>::TM]) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  using K = EpiKind<EPI>;
   constexpr int TM = C::TM, TN = C::TN, WM = C::WM, WN = C::WN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const float gs = (FP4 && p.b_gscale) ? sload(p.b_gscale + g) : 1.0f;
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) {
-    constexpr int U = BN / 8;                      // 16-byte units per staged row
+  // weight scale times activation scale (1 for bf16 operands)
+  const float sc = (p.b_gscale ? sload(p.b_gscale + g) : 1.0f) * (p.a_scale ? sload(p.a_scale) : 1.0f);
+  const float rq = K::Q8 ? 1.0f / sload(p.q_scale) : 1.0f;
+  if constexpr (K::STAGED) {
+    constexpr int EL = K::ELEM;
+    constexpr int RB = BN * EL;                    // staged row bytes
+    constexpr int U = RB / 16;                     // 16-byte units per staged row
     constexpr int ROWS = 32 * WGM;                 // staged rows per i-block
     constexpr int PER = ROWS * U / C::NT;          // units stored per thread
     static_assert(ROWS * U % C::NT == 0, "epilogue units");
     const int lr = wm * 32 + (lane & 31);          // this lane's staged row
     // stores through a buffer resource over the tile's rows: lanes past the
     // tile's last row or column get an out-of-range offset and are dropped by
-    // the hardware, so every thread issues all EPI_STORES stores (the k-loop
-    // waits count them)
+    // the hardware, so every thread issues all PER stores per i-block (the
+    // k-loop waits count them)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (uint16_t*)p.C + (int64_t)r0 * p.ldc, 0, (r1 - r0) * (int)p.ldc * 2, 0x00020000);
+        (char*)p.C + (int64_t)r0 * p.ldc * EL, 0, (r1 - r0) * (int)p.ldc * EL, 0x00020000);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float v0 = acc[j][i][4 * q + 0], v1 = acc[j][i][4 * q + 1];
-          float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
-          if (EPI == EPI_SQRELU_BF16) {
-            v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
-            v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
+          float v0 = acc[j][i][4 * q + 0] * sc, v1 = acc[j][i][4 * q + 1] * sc;
+          float v2 = acc[j][i][4 * q + 2] * sc, v3 = acc[j][i][4 * q + 3] * sc;
+          if (K::SQRELU) {
+            v0 = fmaxf(v0, 0.f); v1 = fmaxf(v1, 0.f); v2 = fmaxf(v2, 0.f); v3 = fmaxf(v3, 0.f);
             v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
-          } else if (FP4) {
-            v0 *= gs; v1 *= gs; v2 *= gs; v3 *= gs;
           }
           const int lc = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-          const int u = (lc >> 3) ^ (lr & (U - 1));
-          *reinterpret_cast<uint2*>(stage + lr * (BN * 2) + u * 16 + (lc & 7) * 2) =
-              make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+          const int cb = lc * EL;                  // byte column in the staged row
+          const int u = (cb >> 4) ^ (lr & (U - 1));
+          char* dst = stage + lr * RB + u * 16 + (cb & 15);
+          if constexpr (EL == 2) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = q8x4(v0, v1, v2, v3, rq);
+          }
         }
       }
       bar_lds();                                   // i-block staged by every wavefront
@@ -363,10 +388,10 @@ __device__ __forceinline__ void epilogue_tile(
       for (int k = 0; k < PER; ++k) {
         const int gidx = threadIdx.x + k * C::NT;
         const int row = gidx / U, un = gidx % U;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + (un ^ (row & (U - 1))) * 16);
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * RB + (un ^ (row & (U - 1))) * 16);
         const int lrow = (row >> 5) * WM + i * 32 + (row & 31);   // row within the tile
-        const int col = n0 + un * 8;
-        const int off = (r0 + lrow < r1 && col < p.N) ? (lrow * (int)p.ldc + col) * 2 : 0x7FFFFFF0;
+        const int col = n0 + un * (16 / EL);
+        const int off = (r0 + lrow < r1 && col < p.N) ? (lrow * (int)p.ldc + col) * EL : 0x7FFFFFF0;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
       }
       bar_lds();                                   // staging free for the next i-block
@@ -386,22 +411,19 @@ __device__ __forceinline__ void epilogue_tile(
           float v2 = acc[j][i][4 * q + 2], v3 = acc[j][i][4 * q + 3];
           const int64_t o = (int64_t)row * p.ldc + col;
           if (EPI == EPI_F32) {
+            v0 *= sc; v1 *= sc; v2 *= sc; v3 *= sc;
             *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
           } else if (EPI == EPI_Z) {
             *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
             *reinterpret_cast<uint2*>((uint16_t*)p.C2 + (int64_t)row * p.ldc2 + col) =
                 make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
-          } else {
-            if (EPI == EPI_BF16_ADD) {
-              const float4 ad = *reinterpret_cast<const float4*>(p.add + (int64_t)row * p.ld_add + col);
-              v0 += ad.x; v1 += ad.y; v2 += ad.z; v3 += ad.w;
-            } else if (EPI == EPI_SQRELU_BF16) {
-              v0 = fmaxf(v0 * gs, 0.f); v1 = fmaxf(v1 * gs, 0.f);
-              v2 = fmaxf(v2 * gs, 0.f); v3 = fmaxf(v3 * gs, 0.f);
-              v0 *= v0; v1 *= v1; v2 *= v2; v3 *= v3;
-            } else {                               // EPI_BF16
-              v0 *= gs; v1 *= gs; v2 *= gs; v3 *= gs;
-            }
+          } else if (EPI == EPI_Z8) {
+            *reinterpret_cast<float4*>((float*)p.C + o) = make_float4(v0, v1, v2, v3);
+            *reinterpret_cast<uint32_t*>((uint8_t*)p.C2 + (int64_t)row * p.ldc2 + col) =
+                q8x4(v0, v1, v2, v3, rq);
+          } else if (EPI == EPI_BF16_ADD) {
+            const float4 ad = *reinterpret_cast<const float4*>(p.add + (int64_t)row * p.ld_add + col);
+            v0 += ad.x; v1 += ad.y; v2 += ad.z; v3 += ad.w;
             *reinterpret_cast<uint2*>((uint16_t*)p.C + o) =
                 make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
           }
@@ -411,52 +433,81 @@ __device__ __forceinline__ void epilogue_tile(
   }
 }
 
-// Operand fragments of one 16-wide k substep for one wavefront.  NVFP4 B
-// fragments stay raw (8 codes and their block scale) until the MFMAs use them.
-template <class C, bool FP4 = C::IS_FP4>
+// Operand fragments of one k substep for one wavefront: 16 bf16 wide, or 64
+// E4M3 codes wide (FP8: each lane's 16 bytes of two consecutive 16-wide bf16
+// substeps).  NVFP4 B fragments stay raw (8 codes and their block scale) until
+// the MFMAs use them.
+template <class C, int W = (C::IS_FP4 ? WT_NVFP4 : C::IS_FP8 ? WT_FP8 : WT_BF16)>
 struct Frags {
   bf16x8 a[C::TM], b[C::TN];
 };
 template <class C>
-struct Frags<C, true> {
+struct Frags<C, WT_NVFP4> {
   bf16x8 a[C::TM];
   uint32_t bq[C::TN], bs[C::TN];
 };
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <class C>
+struct Frags<C, WT_FP8> {
+  i32x8 a[C::TM], b[C::TN];                      // one MFMA operand each (32 codes)
+};
+// two 16-byte LDS chunks -> one 8-dword MFMA operand
+__device__ __forceinline__ i32x8 lds_pair(const uint4* base, int c0, int c1) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + c0);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + c1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // Fragments of substep s of the k-tile in `stage`.  kbyte: position of the
 // k-tile's first scale byte in the aligned scale dword of each row (NVFP4).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
 __device__ __forceinline__ void read_frags(const char* stage, int s, int kbyte,
-                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>>& f) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
+                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& f) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
   constexpr int CPR = C::CPR, WM = C::WM, WN = C::WN;
   const uint4* As = reinterpret_cast<const uint4*>(stage);
+  const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int ch = s * 2 + (lane >> 5);
+  if constexpr (C::IS_FP8) {
+    // step s: 16-byte chunks 4s + h and 4s + 2 + h for lane half h
+    const int c0 = s * 4 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int row = wm * WM + i * 32 + (lane & 31);
-    f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
-  }
-  if constexpr (FP4) {
-    // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
-    // 8(s & 1) + 4h of 32-k chunk s / 2
-    const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
-    const uint8_t* Sc = Q + C::BQ_BYTES;
+    for (int i = 0; i < C::TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      f.a[i] = lds_pair(As + row * CPR, swz_chunk<CPR>(row, c0), swz_chunk<CPR>(row, c0 + 2));
+    }
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       const int n = wn * WN + j * 32 + (lane & 31);
-      f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
-                                                   ((lane >> 5) << 2));
-      f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
+      f.b[j] = lds_pair(Bs + n * CPR, swz_chunk<CPR>(n, c0), swz_chunk<CPR>(n, c0 + 2));
     }
   } else {
-    const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
+    const int ch = s * 2 + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = wn * WN + j * 32 + (lane & 31);
-      f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+    for (int i = 0; i < C::TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
+    }
+    if constexpr (C::FP4) {
+      // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
+      // 8(s & 1) + 4h of 32-k chunk s / 2
+      const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
+      const uint8_t* Sc = Q + C::BQ_BYTES;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = wn * WN + j * 32 + (lane & 31);
+        f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
+                                                     ((lane >> 5) << 2));
+        f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int n = wn * WN + j * 32 + (lane & 31);
+        f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
+      }
     }
   }
 }
@@ -465,14 +516,23 @@ __device__ __forceinline__ void read_frags(const char* stage, int s, int kbyte,
 // B fragments are decoded here, exactly, to bf16.
 template <class C>
 __device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
+  if constexpr (C::IS_FP8) {
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) {
-    bf16x8 b;
-    if constexpr (C::IS_FP4) b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
-    else b = f.b[j];
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
+      for (int i = 0; i < C::TM; ++i)
+        // E4M3 x E4M3 (format selectors 0), no block scales: the unscaled MFMA
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      bf16x8 b;
+      if constexpr (C::IS_FP4) b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
+      else b = f.b[j];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
+    }
   }
 }
 
@@ -481,7 +541,8 @@ __device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN
 // instead of stalling the wavefront before the first of them.
 template <class C>
 __device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int NR = C::TM + (C::IS_FP4 ? 2 : 1) * C::TN, NM = C::TM * C::TN;
+  constexpr int NR = C::IS_FP8 ? 2 * (C::TM + C::TN) : C::TM + (C::IS_FP4 ? 2 : 1) * C::TN;
+  constexpr int NM = C::TM * C::TN;
   constexpr int P = NR < NM ? NR : NM;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
@@ -506,11 +567,11 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 // after them is needed.  NVFP4 stages hold the raw codes and scales; each
 // wavefront decodes the B fragments it multiplies (those of its wavefront
 // column), so the decode runs on the VALU beside the other wavefront's MFMAs.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, bool FP4, int EPI>
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
 __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const int4* list,
                                             int nrt, int first, int step) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, FP4>;
-  constexpr int TM = C::TM, TN = C::TN, S = BK / 16;
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  constexpr int TM = C::TM, TN = C::TN, S = C::IS_FP8 ? BK / 32 : BK / 16;
   static_assert(S % 2 == 0, "substep 0 of every k-tile uses the first register set");
   const int ntn = (p.N + BN - 1) / BN;
   const int total = nrt * ntn;
@@ -523,19 +584,20 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
   {
     int g, r0, r1, n0;
     item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
-    make_src<BM, BN, BK, WGM, WGN, NST, FP4>(p, g, r0, r1, n0, cur);
+    make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, g, r0, r1, n0, cur);
   }
 #pragma unroll
-  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, cur, s, smem + s * C::STAGE);
+  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, s, smem + s * C::STAGE);
   int issued = NST;          // k-tiles of this stream issued so far
   wait_tiles<C::LOADS, NST - 1>(issued - 1);
   bar();
   Frags<C> f0, f1;
   // the aligned scale dword of each row holds k-tile kt's first scale at this byte
   auto kbyte = [](int kt) { return (kt * (BK / 16)) & 3; };
-  read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(smem, 0, 0, f0);
+  read_frags<BM, BN, BK, WGM, WGN, NST, WT>(smem, 0, 0, f0);
   int gt = 0;                // k-tiles of this stream consumed so far
-  constexpr int ST = (EPI == EPI_BF16 || EPI == EPI_SQRELU_BF16) ? C::EPI_STORES : 0;
+  // stores per thread of one staged epilogue (all issued, see epilogue_tile)
+  constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
   int st_tile = -1;          // last k-tile issued before the latest epilogue's stores
 
   for (;;) {
@@ -557,10 +619,10 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
         if (s % 2 == 0) {
-          read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(st, s + 1, kbyte(kt), f1);
+          read_frags<BM, BN, BK, WGM, WGN, NST, WT>(st, s + 1, kbyte(kt), f1);
           mma_frags<C>(f0, acc);
         } else {
-          read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(st, s + 1, kbyte(kt), f0);
+          read_frags<BM, BN, BK, WGM, WGN, NST, WT>(st, s + 1, kbyte(kt), f0);
           mma_frags<C>(f1, acc);
         }
         interleave_reads_mfma<C>();
@@ -573,14 +635,14 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
         const int j = kt + NST;          // refill stage sg with the k-tile NST ahead
         char* fs = smem + sg * C::STAGE;
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, cur, j, fs);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, j, fs);
           ++issued;
         } else if (has_next) {
-          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, FP4>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, FP4>(p, nxt, j - nk, fs);
+          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, nxt, j - nk, fs);
           ++issued;
         }
-        read_frags<BM, BN, BK, WGM, WGN, NST, FP4>(smem + ((gt + 1) % NST) * C::STAGE, 0,
+        read_frags<BM, BN, BK, WGM, WGN, NST, WT>(smem + ((gt + 1) % NST) * C::STAGE, 0,
                                                    kbyte(kt + 1 < nk ? kt + 1 : 0), f0);
       }
       // one call site for the last substep: duplicating it in both branches
@@ -590,7 +652,7 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
       ++gt;
     }
     st_tile = issued - 1;
-    epilogue_tile<BM, BN, BK, WGM, WGN, NST, FP4, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, WT, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
                                                        smem + NST * C::STAGE, acc);
     if (!has_next) break;
     cur = nxt;
@@ -599,13 +661,146 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
   bar_lds();   // every wave is done with the LDS before the caller reuses it
 }
 
+// FP8 operands of step s (64 codes) for MFMA row block i (A) / column block j
+// (B) of this wavefront (see read_frags).
+template <class C, int WGN>
+__device__ __forceinline__ i32x8 read_a8(const char* stage, int s, int i) {
+  constexpr int CPR = C::CPR;
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / WGN;
+  const int row = wm * C::WM + i * 32 + (lane & 31), c0 = s * 4 + (lane >> 5);
+  return lds_pair(reinterpret_cast<const uint4*>(stage) + row * CPR, swz_chunk<CPR>(row, c0),
+                  swz_chunk<CPR>(row, c0 + 2));
+}
+template <class C, int WGN>
+__device__ __forceinline__ i32x8 read_b8(const char* stage, int s, int j) {
+  constexpr int CPR = C::CPR;
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WGN;
+  const int n = wn * C::WN + j * 32 + (lane & 31), c0 = s * 4 + (lane >> 5);
+  return lds_pair(reinterpret_cast<const uint4*>(stage + C::A_BYTES) + n * CPR, swz_chunk<CPR>(n, c0),
+                  swz_chunk<CPR>(n, c0 + 2));
+}
+
+// Scheduling order of one FP8 step: per row block I, its TN MFMAs, then its
+// reads (two ds_read_b128 per operand: A block I and the B blocks j = I mod TM).
+template <class C, int I>
+__device__ __forceinline__ void sched_fp8_rows() {
+  if constexpr (I < C::TM) {
+    constexpr int NB = (C::TN - I + C::TM - 1) / C::TM;
+    __builtin_amdgcn_sched_group_barrier(0x008, C::TN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NB), 0);
+    sched_fp8_rows<C, I + 1>();
+  }
+}
+
+// One FP8 step: the MFMAs of (fa, fb) and, interleaved with them, the reads of
+// the step after it (step sn of `next`): each A fragment is re-read into its
+// own registers right after its last MFMA (row blocks outermost), B into the
+// other buffer fbn.  One A set plus two B sets keep the 8-wavefront 256x256
+// tile within 256 registers per lane.
+template <class C, int WGN>
+__device__ __forceinline__ void step_fp8(f32x16 (&acc)[C::TN][C::TM], i32x8 (&fa)[C::TM],
+                                         const i32x8 (&fb)[C::TN], i32x8 (&fbn)[C::TN],
+                                         const char* next, int sn) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+    fa[i] = read_a8<C, WGN>(next, sn, i);
+#pragma unroll
+    for (int j = i; j < C::TN; j += C::TM) fbn[j] = read_b8<C, WGN>(next, sn, j);
+  }
+  sched_fp8_rows<C, 0>();
+}
+
+// gemm_stream for FP8 operands (two 64-code steps per k-tile, BK = 64 16-bit
+// slots): the same continuous ring, waits and barrier placement, with the
+// register-lean fragment pipeline of step_fp8.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+__device__ __forceinline__ void gemm_stream_fp8(const GemmArgs& p, char* smem, const int4* list,
+                                                int nrt, int first, int step) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT_FP8>;
+  constexpr int TM = C::TM, TN = C::TN;
+  static_assert(BK == 64, "two 64-code steps per k-tile");
+  const int ntn = (p.N + BN - 1) / BN;
+  const int total = nrt * ntn;
+  if (first >= total) return;
+  const int nk = p.K / BK;
+
+  wait_vm<0>();
+  TileSrc<C> cur, nxt;
+  int it = first;
+  {
+    int g, r0, r1, n0;
+    item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
+    make_src<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, g, r0, r1, n0, cur);
+  }
+#pragma unroll
+  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, cur, s, smem + s * C::STAGE);
+  int issued = NST;
+  wait_tiles<C::LOADS, NST - 1>(issued - 1);
+  bar();
+  i32x8 fa[TM], fb0[TN], fb1[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[i] = read_a8<C, WGN>(smem, 0, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb0[j] = read_b8<C, WGN>(smem, 0, j);
+  int gt = 0;
+  constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
+  int st_tile = -1;
+
+  for (;;) {
+    const int itn = it + step;
+    const bool has_next = itn < total;
+    int ng = 0, nr0 = 0, nr1 = 0, nn0 = 0;
+    if (has_next) item_coords<BM, BN>(p, list, nrt, ntn, itn, ng, nr0, nr1, nn0);
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sg = gt % NST;
+      char* st = smem + sg * C::STAGE;
+      step_fp8<C, WGN>(acc, fa, fb0, fb1, st, 1);        // step 0; reads step 1
+      if (kt + 1 < nk || has_next) {
+        wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
+        bar_lds();
+        const int j = kt + NST;
+        if (j < nk) {
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, cur, j, st);
+          ++issued;
+        } else if (has_next) {
+          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, ng, nr0, nr1, nn0, nxt);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, nxt, j - nk, st);
+          ++issued;
+        }
+      }
+      // step 1; reads step 0 of the next k-tile (after the last k-tile of the
+      // last item they read a stale stage and are not used)
+      step_fp8<C, WGN>(acc, fa, fb1, fb0, smem + ((gt + 1) % NST) * C::STAGE, 0);
+      ++gt;
+    }
+    st_tile = issued - 1;
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
+                                                          smem + NST * C::STAGE, acc);
+    if (!has_next) break;
+    cur = nxt;
+    it = itn;
+  }
+  bar_lds();
+}
+
 // Persistent kernel.  Phase 1 walks list 0 (row tiles of height <= BM, or the
 // dense row blocks), phase 2 list 1 (row tiles of height <= BMS: the remainder
 // of each expert's rows) with its own ring.  Block b takes the
 // items of its XCD's slice of each round of gridDim.x items (block b runs on
 // XCD b % 8), so consecutive items (the column tiles of one row tile, then the
 // next row tiles of the same expert) share an L2.
-template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, bool FP4,
+template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, int WT,
           int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   extern __shared__ uint4 smem_u4[];
@@ -613,21 +808,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   const int G = gridDim.x;
   const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
-  gemm_stream<BM, BN, BK1, WGM, WGN, NST1, FP4, EPI>(p, smem, p.tiles, nrt0, base, G);
-  if constexpr (BMS > 0)
-    gemm_stream<BMS, BN, BK2, WGM, WGN, NST2, FP4, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+  if constexpr (WT == WT_FP8) {
+    gemm_stream_fp8<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
+    if constexpr (BMS > 0)
+      gemm_stream_fp8<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+  } else {
+    gemm_stream<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
+    if constexpr (BMS > 0)
+      gemm_stream<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+  }
 }
 
 namespace {
 
-template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, bool FP4,
+template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, int WT,
           int EPI>
 hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t s) {
-  constexpr size_t lds1 = (size_t)TileCfg<BM, BN, BK1, WGM, WGN, NST1, FP4>::LDS;
-  constexpr size_t lds2 = BMS > 0 ? (size_t)TileCfg<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, FP4>::LDS : 0;
+  constexpr size_t lds1 = (size_t)TileCfg<BM, BN, BK1, WGM, WGN, NST1, WT>::LDS;
+  constexpr size_t lds2 = BMS > 0 ? (size_t)TileCfg<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, WT>::LDS : 0;
   constexpr size_t lds = lds1 > lds2 ? lds1 : lds2;
   static_assert(lds <= 160 * 1024, "LDS");
-  auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, FP4, EPI>;
+  auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, WT, EPI>;
   // every stage of the ring holds a k-tile of the first output tile
   if (a.K / BK1 < NST1 || (BMS > 0 && a.K / BK2 < NST2)) return hipErrorInvalidValue;
   static bool attr_set = false;
@@ -648,43 +849,67 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
 
 // bf16: both lists with BK = 64 (fewer barriers per flop; 2 stages for
 // 256x256 tiles, 3 for smaller ones).  NVFP4: BK = 64 with 3 stages (a raw
-// stage is 5/8 of a bf16 one).  Short reductions (K = 64, 128) take rings that
-// fit in K / BK k-tiles.
+// stage is 5/8 of a bf16 one).  FP8 (K in 16-bit slots here): the bf16 rings
+// with BK = 64, whole 64-code MFMA steps.  Short reductions (K = 64, 128) take
+// rings that fit in K / BK k-tiles.
 template <int BM, int BN, int BMS, int WGM, int WGN, int EPI, bool GROUPED>
-hipError_t launch_epi(const GemmArgs& a, bool fp4, int64_t grid, int num_cu, hipStream_t s) {
+hipError_t launch_epi(const GemmArgs& a, int wt, int64_t grid, int num_cu, hipStream_t s) {
   constexpr int NSTB = (BM == 256 && BN == 256) ? 2 : 3;
-  if constexpr (GROUPED) {         // NVFP4 weights: grouped expert GEMMs only
-    if (fp4) {
-      if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, 3, 64, 3, true, EPI>(a, grid, num_cu, s);
-      if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 64, 2, 64, 2, true, EPI>(a, grid, num_cu, s);
-      return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, true, EPI>(a, grid, num_cu, s);
+  constexpr bool Q8OUT = EPI == EPI_Q8 || EPI == EPI_SQRELU_Q8;
+  if constexpr (GROUPED && !Q8OUT) {   // NVFP4 weights: grouped expert GEMMs only
+    if (wt == WT_NVFP4) {
+      if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, 3, 64, 3, WT_NVFP4, EPI>(a, grid, num_cu, s);
+      if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 64, 2, 64, 2, WT_NVFP4, EPI>(a, grid, num_cu, s);
+      return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, WT_NVFP4, EPI>(a, grid, num_cu, s);
     }
   }
-  if (fp4) return hipErrorInvalidValue;
-  if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, NSTB, 64, NSTB, false, EPI>(a, grid, num_cu, s);
-  if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 32, 4, 32, 4, false, EPI>(a, grid, num_cu, s);
-  return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, false, EPI>(a, grid, num_cu, s);
+  if (wt == WT_NVFP4) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_SQRELU_Q8 || EPI == EPI_BF16 || EPI == EPI_F32) {
+    if (wt == WT_FP8) {
+      if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, NSTB, 64, NSTB, WT_FP8, EPI>(a, grid, num_cu, s);
+      if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 64, 2, 64, 2, WT_FP8, EPI>(a, grid, num_cu, s);
+      return hipErrorInvalidValue;
+    }
+  }
+  if (wt != WT_BF16) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_SQRELU_Q8) {
+    return hipErrorInvalidValue;       // quantised hidden rows only from FP8 GEMMs
+  } else {
+    if (a.K >= 192) return launch_one<BM, BN, BMS, WGM, WGN, 64, NSTB, 64, NSTB, WT_BF16, EPI>(a, grid, num_cu, s);
+    if (a.K == 128) return launch_one<BM, BN, BMS, WGM, WGN, 32, 4, 32, 4, WT_BF16, EPI>(a, grid, num_cu, s);
+    return launch_one<BM, BN, BMS, WGM, WGN, 32, 2, 32, 2, WT_BF16, EPI>(a, grid, num_cu, s);
+  }
 }
 
 template <int BM, int BN, int BMS, int WGM, int WGN>
-hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int num_cu, hipStream_t s) {
-  if (a.tiles) {                   // grouped expert GEMMs: bf16 or NVFP4 weights
+hipError_t launch_shape(const GemmArgs& a, int wt, int epi, int64_t grid, int num_cu, hipStream_t s) {
+  if (a.tiles) {                   // grouped expert GEMMs: bf16, NVFP4 or FP8 weights
     if constexpr (BMS > 0) {
       switch (epi) {
-        case EPI_SQRELU_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_SQRELU_BF16, true>(a, fp4, grid, num_cu, s);
-        case EPI_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_BF16, true>(a, fp4, grid, num_cu, s);
+        case EPI_SQRELU_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_SQRELU_BF16, true>(a, wt, grid, num_cu, s);
+        case EPI_BF16: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_BF16, true>(a, wt, grid, num_cu, s);
+        case EPI_SQRELU_Q8: return launch_epi<BM, BN, BMS, WGM, WGN, EPI_SQRELU_Q8, true>(a, wt, grid, num_cu, s);
         default: break;
       }
     }
     return hipErrorInvalidValue;
   }
-  if (fp4 || BMS != 0) return hipErrorInvalidValue;   // dense GEMMs: bf16 weights, no lists
+  if (wt == WT_NVFP4 || BMS != 0) return hipErrorInvalidValue;   // dense GEMMs: no lists
+  if (wt == WT_FP8) {              // FP8 dense GEMMs: the shared experts
+    switch (epi) {
+      case EPI_SQRELU_Q8: return launch_epi<BM, BN, 0, WGM, WGN, EPI_SQRELU_Q8, false>(a, wt, grid, num_cu, s);
+      case EPI_F32: return launch_epi<BM, BN, 0, WGM, WGN, EPI_F32, false>(a, wt, grid, num_cu, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
-    case EPI_SQRELU_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_SQRELU_BF16, false>(a, false, grid, num_cu, s);
-    case EPI_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16, false>(a, false, grid, num_cu, s);
-    case EPI_Z: return launch_epi<BM, BN, 0, WGM, WGN, EPI_Z, false>(a, false, grid, num_cu, s);
-    case EPI_F32: return launch_epi<BM, BN, 0, WGM, WGN, EPI_F32, false>(a, false, grid, num_cu, s);
-    case EPI_BF16_ADD: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16_ADD, false>(a, false, grid, num_cu, s);
+    case EPI_SQRELU_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_SQRELU_BF16, false>(a, wt, grid, num_cu, s);
+    case EPI_BF16: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16, false>(a, wt, grid, num_cu, s);
+    case EPI_Z: return launch_epi<BM, BN, 0, WGM, WGN, EPI_Z, false>(a, wt, grid, num_cu, s);
+    case EPI_Z8: return launch_epi<BM, BN, 0, WGM, WGN, EPI_Z8, false>(a, wt, grid, num_cu, s);
+    case EPI_Q8: return launch_epi<BM, BN, 0, WGM, WGN, EPI_Q8, false>(a, wt, grid, num_cu, s);
+    case EPI_F32: return launch_epi<BM, BN, 0, WGM, WGN, EPI_F32, false>(a, wt, grid, num_cu, s);
+    case EPI_BF16_ADD: return launch_epi<BM, BN, 0, WGM, WGN, EPI_BF16_ADD, false>(a, wt, grid, num_cu, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -694,19 +919,28 @@ hipError_t launch_shape(const GemmArgs& a, bool fp4, int epi, int64_t grid, int 
 // Tile shapes: 256x256 (8 wavefronts, 2x4), 256x128 and 128x128 (4 wavefronts,
 // 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height
 // bm, list 1 of height bms; max_items bounds the items for the grid size.
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool b_nvfp4, int epi, int bm, int bn, int bms,
+hipError_t launch_gemm_bf16(const GemmArgs& a0, int wt, int epi, int bm, int bn, int bms,
                             int64_t max_items, int num_cu, hipStream_t s) {
-  if (!a.tiles && bms != 0) return hipErrorInvalidValue;
+  if (!a0.tiles && bms != 0) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  if (wt == WT_FP8) {
+    // two codes per 16-bit slot: the loads and the LDS layout of a bf16 GEMM
+    // over K / 2
+    if ((a.K | a.lda | a.ldb | a.b_gstride) & 1) return hipErrorInvalidValue;
+    if (a.kseg < a.K && ((a.kseg | a.b_segstride) & 1)) return hipErrorInvalidValue;
+    a.K /= 2; a.lda /= 2; a.ldb /= 2; a.b_gstride /= 2;
+    if (a0.kseg < a0.K) { a.kseg /= 2; a.b_segstride /= 2; }
+  }
   const int64_t total = a.tiles ? max_items
                                 : (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   if (!a.tiles) {
-    if (bm == 256 && bn == 256) return launch_shape<256, 256, 0, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
-    if (bm == 256 && bn == 128) return launch_shape<256, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
-    if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
+    if (bm == 256 && bn == 256) return launch_shape<256, 256, 0, 2, 4>(a, wt, epi, total, num_cu, s);
+    if (bm == 256 && bn == 128) return launch_shape<256, 128, 0, 2, 2>(a, wt, epi, total, num_cu, s);
+    if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, wt, epi, total, num_cu, s);
     return hipErrorInvalidValue;
   }
-  if (bm == 256 && bn == 256 && bms == 128) return launch_shape<256, 256, 128, 2, 4>(a, b_nvfp4, epi, total, num_cu, s);
-  if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, b_nvfp4, epi, total, num_cu, s);
+  if (bm == 256 && bn == 256 && bms == 128) return launch_shape<256, 256, 128, 2, 4>(a, wt, epi, total, num_cu, s);
+  if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, wt, epi, total, num_cu, s);
   return hipErrorInvalidValue;
 }
 

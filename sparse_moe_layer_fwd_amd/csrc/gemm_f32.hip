@@ -128,7 +128,9 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_
   return hipGetLastError();
 }
 
-// out[r][c] = epi( sum_{s=0..ks-1} P[s][r][c] ), summed in that fixed order.
+// out[r][c] = epi( g * sum_{s=0..ks-1} P[s][r][c] ), summed in that fixed
+// order; g = the weight scale b_gscale[0] times the activation scale *a_scale
+// (FP8 dense GEMMs), 1 where absent.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int ks, int M,
                                                             int N, GemmArgs p) {
@@ -137,6 +139,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
   float v = 0.0f;
   for (int k = 0; k < ks; ++k) v += P[(int64_t)k * M * N + i];
+  v *= (p.b_gscale ? p.b_gscale[0] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f);
+  const float rq = (EPI == EPI_Z8 || EPI == EPI_Q8 || EPI == EPI_SQRELU_Q8) ? 1.0f / *p.q_scale : 1.0f;
   if (EPI == EPI_F32) {
     if (p.bias) v += p.bias[col];
     ((float*)p.C)[(int64_t)row * p.ldc + col] = v;
@@ -155,6 +159,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   } else if (EPI == EPI_SQRELU_BF16) {
     v = fmaxf(v, 0.0f);
     ((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(v * v);
+  } else if (EPI == EPI_Z8) {
+    ((float*)p.C)[(int64_t)row * p.ldc + col] = v;
+    ((uint8_t*)p.C2)[(int64_t)row * p.ldc2 + col] = (uint8_t)q8(v, rq);
+  } else if (EPI == EPI_Q8) {
+    ((uint8_t*)p.C)[(int64_t)row * p.ldc + col] = (uint8_t)q8(v, rq);
+  } else if (EPI == EPI_SQRELU_Q8) {
+    v = fmaxf(v, 0.0f);
+    ((uint8_t*)p.C)[(int64_t)row * p.ldc + col] = (uint8_t)q8(v * v, rq);
   }
 }
 
@@ -169,6 +181,9 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float*
     case EPI_BF16: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16>, g, b, 0, s, P, ks, a.M, a.N, a); break;
     case EPI_BF16_ADD: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_BF16_ADD>, g, b, 0, s, P, ks, a.M, a.N, a); break;
     case EPI_SQRELU_BF16: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SQRELU_BF16>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_Z8: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_Z8>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_Q8: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_Q8>, g, b, 0, s, P, ks, a.M, a.N, a); break;
+    case EPI_SQRELU_Q8: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SQRELU_Q8>, g, b, 0, s, P, ks, a.M, a.N, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

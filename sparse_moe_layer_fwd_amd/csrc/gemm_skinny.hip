@@ -8,11 +8,13 @@
 //
 // Grid: (column tiles of 64, experts).  A block owns 64 output columns of one
 // expert; its 4 wavefronts split the reduction dimension in four and reduce
-// through LDS at the end.  Per step a lane loads 32 contiguous bytes of one
-// weight row (16 bf16, or 16 NVFP4 codes + their block scale) and the matching
-// 16 activations of each row block, and issues two v_mfma_f32_16x16x32_bf16 per
-// (row block, column block).  Both operands use the same permutation of the
-// reduction index inside a step, which leaves the dot products unchanged.
+// through LDS at the end.  Per step a lane loads 16 contiguous elements of one
+// weight row (16 bf16, 16 NVFP4 codes + their block scale, or 16 E4M3 codes)
+// and the matching 16 activations of each row block (bf16, or E4M3 codes with
+// FP8 weights), decodes codes exactly to bf16, and issues two
+// v_mfma_f32_16x16x32_bf16 per (row block, column block).  Both operands use
+// the same permutation of the reduction index inside a step, which leaves the
+// dot products unchanged.
 #include <string.h>
 
 #include "common.h"
@@ -30,23 +32,25 @@ __device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
 // Rows [row0, row0 + cnt) (cnt <= 64) of expert e, columns [n0, n0 + 64).
 // K range [kbeg, kbeg + klen) (klen a multiple of 256): each wavefront takes a
 // quarter.
-template <bool FP4, int EPI>
+template <int WT, int EPI>
 __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[16][4][64], int e,
                                              int row0, int cnt, int n0, int kbeg, int klen) {
+  constexpr bool FP4 = WT == WT_NVFP4, FP8 = WT == WT_FP8;
+  constexpr int AEL = FP8 ? 1 : 2;                       // activation element bytes
   constexpr int MAXRB = 4;
   const int nrb = (cnt + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = klen >> 2;
   const int kw0 = kbeg + wave * kq;
   const int grp = lane >> 4;                             // which 16-wide k slice of a 64-step
-  const uint16_t* arow[MAXRB];
+  const char* arow[MAXRB];
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
     const int r = rb * 16 + (lane & 15);
     if (r < cnt) {
       const int lr = row0 + r;
       const int64_t pr = p.a_rows ? (int64_t)p.a_rows[lr] : (int64_t)lr;
-      arow[rb] = p.A + pr * p.lda;
+      arow[rb] = (const char*)p.A + pr * p.lda * AEL;
     } else {
       arow[rb] = nullptr;
     }
@@ -59,6 +63,9 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
     if (FP4) {
       brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb;
       srow[cb] = p.b_scale + (int64_t)e * p.s_gstride + (int64_t)n * p.lds_scale;
+    } else if (FP8) {
+      brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb;
+      srow[cb] = nullptr;
     } else {
       brow[cb] = (const uint8_t*)((const uint16_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb);
       srow[cb] = nullptr;
@@ -84,6 +91,10 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
                               fp4x2_bf((c.x >> 16) & 0xFFu, s), fp4x2_bf(c.x >> 24, s));
         b[cb][1] = make_uint4(fp4x2_bf(c.y & 0xFFu, s), fp4x2_bf((c.y >> 8) & 0xFFu, s),
                               fp4x2_bf((c.y >> 16) & 0xFFu, s), fp4x2_bf(c.y >> 24, s));
+      } else if (FP8) {
+        const uint4 c = *reinterpret_cast<const uint4*>(brow[cb] + k);
+        b[cb][0] = e4m3x8_bf(c.x, c.y);
+        b[cb][1] = e4m3x8_bf(c.z, c.w);
       } else {
         const uint4* q = reinterpret_cast<const uint4*>((const uint16_t*)brow[cb] + k);
         b[cb][0] = q[0];
@@ -95,9 +106,15 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
       if (rb < nrb) {
         uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
         if (arow[rb]) {
-          const uint4* q = reinterpret_cast<const uint4*>(arow[rb] + k);
-          a0 = q[0];
-          a1 = q[1];
+          const uint4* q = reinterpret_cast<const uint4*>(arow[rb] + k * AEL);
+          if (FP8) {
+            const uint4 c = q[0];
+            a0 = e4m3x8_bf(c.x, c.y);
+            a1 = e4m3x8_bf(c.z, c.w);
+          } else {
+            a0 = q[0];
+            a1 = q[1];
+          }
         }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
@@ -122,7 +139,9 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
   }
   __syncthreads();
   if (wave != 0) return;                                // the caller re-syncs every wavefront
-  const float gs = (FP4 && p.b_gscale) ? p.b_gscale[e] : 1.0f;
+  // weight scale times activation scale (1 for bf16 operands)
+  const float sc = (p.b_gscale ? p.b_gscale[e] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f);
+  const float rq = EPI == EPI_SQRELU_Q8 ? 1.0f / *p.q_scale : 1.0f;
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
     if (rb >= nrb) continue;
@@ -141,8 +160,13 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
           p.P[(int64_t)blockIdx.y * p.p_slice + orow * p.N + col] = v;
           continue;
         }
-        v *= gs;
-        uint16_t* C = p.C + orow * p.ldc + col;
+        v *= sc;
+        if (EPI == EPI_SQRELU_Q8) {
+          const float h = fmaxf(v, 0.0f);
+          ((uint8_t*)p.C)[orow * p.ldc + col] = (uint8_t)q8(h * h, rq);
+          continue;
+        }
+        uint16_t* C = (uint16_t*)p.C + orow * p.ldc + col;
         if (EPI == EPI_SQRELU_BF16) {
           const float h = fmaxf(v, 0.0f);
           *C = (uint16_t)f2bf(h * h);
@@ -157,7 +181,7 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 // Grid (column tiles of 64, experts).  An expert with 0 < count < max_rows is
 // processed in chunks of up to 64 rows; larger experts are left to the tiled
 // GEMM.
-template <bool FP4, int EPI>
+template <int WT, int EPI>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   __shared__ float red[3][16][4][64];                    // partial sums of waves 1..3
   const int e = blockIdx.y;
@@ -165,7 +189,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   if (cnt == 0 || cnt >= p.max_rows) return;
   const int row0 = p.offs[e];
   for (int c0 = 0; c0 < cnt; c0 += 64) {
-    skinny_chunk<FP4, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
+    skinny_chunk<WT, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
     __syncthreads();
   }
 }
@@ -173,39 +197,47 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 // Dense split-K: grid (N / 64, ks, row chunks of 64).  Block (x, y, z) sums
 // rows [64 z, 64 z + 64) x columns [64 x, 64 x + 64) over K slice y into the
 // fp32 partials P[y].
+template <int WT>
 __global__ __launch_bounds__(256) void skinny_dense_kernel(SkinnyArgs p, int M) {
   __shared__ float red[3][16][4][64];
   const int kl = p.K / (int)gridDim.y;
   const int row0 = blockIdx.z * 64;
-  skinny_chunk<false, EPI_PARTIAL>(p, red, 0, row0, min(64, M - row0), blockIdx.x * 64,
-                                   (int)blockIdx.y * kl, kl);
+  skinny_chunk<WT, EPI_PARTIAL>(p, red, 0, row0, min(64, M - row0), blockIdx.x * 64,
+                                (int)blockIdx.y * kl, kl);
 }
 
-hipError_t launch_skinny_splitk(const GemmArgs& a, int epi, int ks, float* P, hipStream_t s) {
+hipError_t launch_skinny_splitk(const GemmArgs& a, bool fp8, int epi, int ks, float* P, hipStream_t s) {
   if (a.tiles || ks < 1 || a.K % (256 * ks) != 0 || a.N % 64 != 0 || a.kseg < a.K) return hipErrorInvalidValue;
   SkinnyArgs k;
   memset(&k, 0, sizeof(k));
-  k.A = (const uint16_t*)a.A; k.lda = a.lda; k.a_rows = nullptr;
+  k.A = a.A; k.lda = a.lda; k.a_rows = nullptr;
   k.B = a.B; k.ldb = a.ldb; k.b_gstride = 0;
   k.N = a.N; k.K = a.K;
   k.P = P; k.p_slice = (int64_t)a.M * a.N;
   dim3 g(a.N / 64, ks, (a.M + 63) / 64), b(256);
-  hipLaunchKernelGGL(skinny_dense_kernel, g, b, 0, s, k, a.M);
+  if (fp8) hipLaunchKernelGGL(skinny_dense_kernel<WT_FP8>, g, b, 0, s, k, a.M);
+  else hipLaunchKernelGGL(skinny_dense_kernel<WT_BF16>, g, b, 0, s, k, a.M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(a, epi, ks, P, s);
 }
 
-hipError_t launch_skinny(const SkinnyArgs& a, bool b_nvfp4, int epi, int n_experts, hipStream_t s) {
+hipError_t launch_skinny(const SkinnyArgs& a, int wt, int epi, int n_experts, hipStream_t s) {
   dim3 g((a.N + 63) / 64, n_experts), b(256);
-  if (b_nvfp4) {
-    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_SQRELU_BF16>), g, b, 0, s, a);
-    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<true, EPI_BF16>), g, b, 0, s, a);
+  if (wt == WT_NVFP4) {
+    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<WT_NVFP4, EPI_SQRELU_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_NVFP4, EPI_BF16>), g, b, 0, s, a);
+    else return hipErrorInvalidValue;
+  } else if (wt == WT_FP8) {
+    if (epi == EPI_SQRELU_Q8) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_SQRELU_Q8>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_BF16>), g, b, 0, s, a);
+    else return hipErrorInvalidValue;
+  } else if (wt == WT_BF16) {
+    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<WT_BF16, EPI_SQRELU_BF16>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_BF16, EPI_BF16>), g, b, 0, s, a);
     else return hipErrorInvalidValue;
   } else {
-    if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_SQRELU_BF16>), g, b, 0, s, a);
-    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<false, EPI_BF16>), g, b, 0, s, a);
-    else return hipErrorInvalidValue;
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

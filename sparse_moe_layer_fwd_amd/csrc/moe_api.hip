@@ -40,6 +40,7 @@ constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> sk
 constexpr size_t kPartialPerCu = 2 * 64 * 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // ---- optional stage timing: a HIP event pair around each stage ----
 struct Prof {
@@ -92,14 +93,21 @@ struct StageScope {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Plan {
-  size_t z32, z16, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
-  size_t slot_token, tk_slot, H, O, u, Hs, ys, partial, total;
+  size_t z32, z16, z8, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
+  size_t slot_token, tk_slot, H, O, u, x8, Hs, ys, partial, total;
   int nchunks, bm, bms, max_tiles, max_tiles2;
   int cold;        // prefill: experts with fewer rows go to the skinny kernel (0: none)
   bool f32, skinny;
+  bool fp8;        // FP8 routed experts: E4M3 latent rows z8 and hidden rows H
+  bool sfp8;       // FP8 shared experts: E4M3 x8 and hidden rows Hs
 };
 
 bool use_f32(const moe_config_t& c) { return c.act_dtype == MOE_F32; }
+
+// weight storage of the routed experts' GEMMs
+int expert_wt(const moe_config_t& c) {
+  return c.expert_dtype == MOE_NVFP4 ? WT_NVFP4 : c.expert_dtype == MOE_FP8 ? WT_FP8 : WT_BF16;
+}
 
 bool use_skinny(const moe_config_t& c, int T) {
   return !use_f32(c) && T <= kSkinnyMaxT && c.latent % 256 == 0 && c.ffn % 256 == 0;
@@ -112,7 +120,11 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
   const size_t L = (size_t)c.latent, M = (size_t)c.ffn, D = (size_t)c.d;
   p.f32 = use_f32(c);
   p.skinny = use_skinny(c, T);
+  p.fp8 = c.expert_dtype == MOE_FP8;
+  p.sfp8 = c.n_shared > 0 && c.shared_fp8;
   const size_t es = p.f32 ? 4 : 2;
+  const size_t esh = p.fp8 ? 1 : es;                 // expert hidden rows H
+  const size_t ess = p.sfp8 ? 1 : es;                // shared hidden rows Hs
   p.nchunks = (T + kTokensPerChunk - 1) / kTokensPerChunk;
   if (p.f32) {
     p.bm = kF32BM;
@@ -138,8 +150,10 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
   }
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes); return at; };
-  p.z32 = take(c.has_latent_proj ? Tz * L * 4 : 0);
-  p.z16 = take(c.has_latent_proj && !p.f32 ? Tz * L * 2 : 0);
+  // z32 feeds the router (unless it reads x); z16 or z8 the experts
+  p.z32 = take(c.has_latent_proj && (p.f32 || !c.router_on_x) ? Tz * L * 4 : 0);
+  p.z16 = take(c.has_latent_proj && !p.f32 && !p.fp8 ? Tz * L * 2 : 0);
+  p.z8 = take(p.fp8 ? Tz * L : 0);
   p.logits = take(Tz * N * 4);
   p.idx = take(Tz * K * 4);
   p.gate = take(Tz * K * 4);
@@ -154,10 +168,11 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
   // aligned groups of up to 16 with scalar loads and discards those past the tile
   p.slot_token = take(Tz * K * 4 + 64);
   p.tk_slot = take(Tz * K * 4);
-  p.H = take(Tz * K * M * es);
+  p.H = take(Tz * K * M * esh);
   p.O = take(Tz * K * L * es);
   p.u = take(c.has_latent_proj ? Tz * L * es : 0);
-  p.Hs = take(c.n_shared ? Tz * (size_t)c.n_shared * c.shared_ffn * es : 0);
+  p.x8 = take(p.sfp8 ? Tz * D : 0);
+  p.Hs = take(c.n_shared ? Tz * (size_t)c.n_shared * c.shared_ffn * ess : 0);
   p.ys = take(c.n_shared ? Tz * D * 4 : 0);
   // split-K partial sums of the dense GEMMs whose output tiles cannot fill the
   // device (small batches); the split factors keep them within this bound
@@ -192,15 +207,17 @@ int split_factor(int64_t tiles, int K, int kstep, int min_slice, int num_cu) {
 // Dense bf16 GEMM.  Small batches (M <= 64) run on the skinny kernel with K
 // split across blocks (weights streamed by every CU); larger ones on the
 // largest tile that still gives every CU work.
-hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, float* P, hipStream_t s) {
+// fp8: A and B are E4M3 codes (the shared experts of an FP8 layer).
+hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, float* P, hipStream_t s,
+                      bool fp8 = false) {
   if (a.M <= 64 && a.N % 64 == 0 && a.K % 256 == 0 && a.kseg >= a.K) {
     const int ks = split_factor(a.N / 64, a.K, 256, 256, num_cu);
     if ((size_t)ks * a.M * a.N <= kPartialPerCu * (size_t)num_cu)   // always, unless N is huge
-      return launch_skinny_splitk(a, epi, ks, P, s);
+      return launch_skinny_splitk(a, fp8, epi, ks, P, s);
   }
   int bm, bn;
   dense_shape(a.M, a.N, num_cu, &bm, &bn);
-  return launch_gemm_bf16(a, false, epi, bm, bn, 0, 0, num_cu, s);
+  return launch_gemm_bf16(a, fp8 ? WT_FP8 : WT_BF16, epi, bm, bn, 0, 0, num_cu, s);
 }
 
 // Dense fp32 GEMM (the router, and every dense GEMM of an all-fp32 layer),
@@ -248,6 +265,16 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
     a.C = at<void>(ws, p.z32); a.ldc = c.latent;
     if (p.f32) {
       MOE_TRY(dense_f32(a, false, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
+    } else if (p.fp8) {
+      // the experts read E4M3 latent rows quantised with their input scale
+      a.q_scale = w.act_scale;
+      if (c.router_on_x) {
+        a.C = at<void>(ws, p.z8);
+        MOE_TRY(dense_bf16(a, EPI_Q8, h->num_cu, at<float>(ws, p.partial), s));
+      } else {
+        a.C2 = at<void>(ws, p.z8); a.ldc2 = c.latent;
+        MOE_TRY(dense_bf16(a, EPI_Z8, h->num_cu, at<float>(ws, p.partial), s));
+      }
     } else if (c.router_on_x) {
       // the router reads x, so only the experts' bf16 latent rows are needed
       a.C = at<void>(ws, p.z16);
@@ -297,17 +324,21 @@ int copy_out(moe_handle_t h, int T, const void* ws, const Plan& p, int32_t* idx,
 }
 
 // One grouped expert GEMM (up: sqrelu epilogue; down: plain, gates are applied by
-// the combine).
+// the combine).  FP8: the up GEMM writes E4M3 hidden rows quantised with the
+// down GEMM's input scale.
 int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const void* A,
                         const int* a_rows, void* C, hipStream_t s) {
   const moe_config_t& c = h->c;
   const moe_weights_t& w = h->w;
   const int64_t rows = up ? c.ffn : c.latent;     // output columns
   const int64_t kdim = up ? c.latent : c.ffn;     // reduction
-  const bool fp4 = c.expert_dtype == MOE_NVFP4;
+  const int wt = expert_wt(c);
+  const bool fp4 = wt == WT_NVFP4, fp8 = wt == WT_FP8;
   const void* B = up ? w.w1 : w.w2;
   const uint8_t* S = up ? w.w1_scale : w.w2_scale;
-  const float* G = up ? w.w1_gscale : w.w2_gscale;
+  const float* G = (fp4 || fp8) ? (up ? w.w1_gscale : w.w2_gscale) : nullptr;
+  const float* as = fp8 ? w.act_scale + (up ? 0 : 1) : nullptr;   // scale of this GEMM's input
+  const float* qs = fp8 && up ? w.act_scale + 1 : nullptr;        // scale of its E4M3 output
   const int cap = h->num_cu * 2;
   StageScope sc(up ? MOE_STAGE_EXPERT_UP : MOE_STAGE_EXPERT_DOWN, s);
   SkinnyArgs sk;
@@ -317,14 +348,14 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   sk.ldb = fp4 ? kdim / 2 : kdim;
   sk.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
   sk.b_scale = S; sk.lds_scale = kdim / 16; sk.s_gstride = rows * kdim / 16;
-  sk.b_gscale = G;
+  sk.b_gscale = G; sk.a_scale = as; sk.q_scale = qs;
   sk.N = (int)rows; sk.K = (int)kdim;
   sk.counts = at<int>(ws, p.counts); sk.offs = at<int>(ws, p.offs);
   sk.max_rows = p.skinny ? INT32_MAX : p.cold;
-  sk.C = (uint16_t*)C; sk.ldc = rows;
-  const int epi = up ? EPI_SQRELU_BF16 : EPI_BF16;
+  sk.C = C; sk.ldc = rows;
+  const int epi = up ? (fp8 ? EPI_SQRELU_Q8 : EPI_SQRELU_BF16) : EPI_BF16;
   if (p.skinny) {
-    MOE_TRY(launch_skinny(sk, fp4, epi, c.n_experts, s));
+    MOE_TRY(launch_skinny(sk, wt, epi, c.n_experts, s));
     return MOE_OK;
   }
   GemmArgs a = gemm_args();
@@ -333,7 +364,7 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   a.ldb = fp4 ? kdim / 2 : kdim;
   a.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
   a.b_scale = S; a.lds_scale = kdim / 16; a.s_gstride = rows * kdim / 16;
-  a.b_gscale = G;
+  a.b_gscale = G; a.a_scale = as; a.q_scale = qs;
   a.N = (int)rows; a.K = (int)kdim;
   a.tiles = at<int4>(ws, p.tiles); a.n_tiles = at<int>(ws, p.ntiles);
   a.tiles2 = at<int4>(ws, p.tiles2);
@@ -346,8 +377,8 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   const int bn = p.bm == 256 ? 256 : 128;
   const int64_t ntn = (rows + bn - 1) / bn;
   const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
-  MOE_TRY(launch_gemm_bf16(a, fp4, epi, p.bm, bn, p.bms, items, h->num_cu, s));
-  if (p.cold > 0) MOE_TRY(launch_skinny(sk, fp4, epi, c.n_experts, s));
+  MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+  if (p.cold > 0) MOE_TRY(launch_skinny(sk, wt, epi, c.n_experts, s));
   return MOE_OK;
 }
 
@@ -379,12 +410,21 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
   if (!c.has_latent_proj && c.latent != c.d) return MOE_ERR_INVALID_ARG;
   if ((int64_t)c.max_tokens * c.top_k > (1 << 30)) return MOE_ERR_INVALID_ARG;
   if (c.act_dtype != MOE_F32 && c.act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (c.expert_dtype != MOE_F32 && c.expert_dtype != MOE_BF16 && c.expert_dtype != MOE_NVFP4)
+  if (c.expert_dtype != MOE_F32 && c.expert_dtype != MOE_BF16 && c.expert_dtype != MOE_NVFP4 &&
+      c.expert_dtype != MOE_FP8)
     return MOE_ERR_INVALID_ARG;
+  if (c.shared_fp8 != 0 && c.shared_fp8 != 1) return MOE_ERR_INVALID_ARG;
+  if (c.shared_fp8 && c.n_shared == 0) return MOE_ERR_INVALID_ARG;
   if (c.n_experts > 1024 || c.top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c.d % 64 || c.latent % 64 || c.ffn % 64 || (c.n_shared && c.shared_ffn % 64))
     return MOE_ERR_UNSUPPORTED;
   if ((c.act_dtype == MOE_F32) != (c.expert_dtype == MOE_F32)) return MOE_ERR_UNSUPPORTED;
+  // FP8 GEMMs run whole 128-code k-tiles, at least two of them
+  if (c.expert_dtype == MOE_FP8 && (c.latent % 128 || c.ffn % 128 || c.latent < 256 || c.ffn < 256))
+    return MOE_ERR_UNSUPPORTED;
+  if (c.shared_fp8 && (c.act_dtype != MOE_BF16 || c.d % 128 || c.shared_ffn % 128 || c.d < 256 ||
+                       c.n_shared * c.shared_ffn < 256))
+    return MOE_ERR_UNSUPPORTED;
   // weights
   if (!w->w_router || !aligned16(w->w_router) || !w->w1 || !aligned16(w->w1) || !w->w2 ||
       !aligned16(w->w2))
@@ -399,8 +439,18 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
         !aligned16(w->w1_scale) || !aligned16(w->w2_scale))
       return MOE_ERR_INVALID_ARG;
   }
+  if (c.expert_dtype == MOE_FP8) {
+    if (!w->w1_gscale || !w->w2_gscale || !w->act_scale || !aligned4(w->w1_gscale) ||
+        !aligned4(w->w2_gscale) || !aligned4(w->act_scale))
+      return MOE_ERR_INVALID_ARG;
+  }
   if (c.n_shared) {
     if (!w->ws1 || !aligned16(w->ws1) || !w->ws2 || !aligned16(w->ws2)) return MOE_ERR_INVALID_ARG;
+  }
+  if (c.shared_fp8) {
+    if (!w->ws1_scale || !w->ws2_scale || !w->shared_act_scale || !aligned4(w->ws1_scale) ||
+        !aligned4(w->ws2_scale) || !aligned4(w->shared_act_scale))
+      return MOE_ERR_INVALID_ARG;
   }
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
@@ -462,8 +512,17 @@ int moe_profile_read(int32_t* launches, double* ms) {
 const char* moe_stage_name(int stage) {
   static const char* names[MOE_NUM_STAGES] = {"down_proj", "router", "topk", "scan", "scatter",
                                               "expert_up", "expert_down", "shared", "combine",
-                                              "up_proj"};
+                                              "up_proj", "quant_x"};
   return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "unknown";
+}
+
+int moe_quantize_fp8(const void* in, int64_t n, const float* scale, uint8_t* out, void* stream) {
+  if (n < 0 || n % 16 != 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!in || !out || !scale || !aligned16(in) || !aligned16(out) || !aligned4(scale))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_quant_fp8((const uint16_t*)in, n, scale, out, (hipStream_t)stream));
+  return MOE_OK;
 }
 
 int moe_destroy(moe_handle_t h) {
@@ -504,9 +563,15 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
                            at<int>(ws, p.tk_slot), s));
   }
   // expert FFNs over expert-sorted rows
-  const void* zsrc = c.has_latent_proj ? (p.f32 ? (const void*)at<float>(ws, p.z32)
-                                                : (const void*)at<uint16_t>(ws, p.z16))
-                                       : x;
+  if (p.fp8 && !c.has_latent_proj) {
+    // no projection writes the experts' E4M3 input rows: quantise x
+    StageScope sc(MOE_STAGE_QUANT, s);
+    MOE_TRY(launch_quant_fp8((const uint16_t*)x, (int64_t)T * c.d, w.act_scale, at<uint8_t>(ws, p.z8), s));
+  }
+  const void* zsrc = p.fp8 ? (const void*)at<uint8_t>(ws, p.z8)
+                     : c.has_latent_proj ? (p.f32 ? (const void*)at<float>(ws, p.z32)
+                                                  : (const void*)at<uint16_t>(ws, p.z16))
+                                         : x;
   st = enqueue_expert_gemm(h, p, ws, true, zsrc, at<int>(ws, p.slot_token), at<void>(ws, p.H), s);
   if (st != MOE_OK) return st;
   st = enqueue_expert_gemm(h, p, ws, false, at<void>(ws, p.H), nullptr, at<void>(ws, p.O), s);
@@ -516,21 +581,27 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
   if (c.n_shared) {
     StageScope sc(MOE_STAGE_SHARED, s);
     const int sm = c.n_shared * c.shared_ffn;
+    if (p.sfp8)
+      MOE_TRY(launch_quant_fp8((const uint16_t*)x, (int64_t)T * c.d, w.shared_act_scale,
+                               at<uint8_t>(ws, p.x8), s));
     GemmArgs a = gemm_args();
-    a.A = x; a.lda = c.d;
+    a.A = p.sfp8 ? (const void*)at<uint8_t>(ws, p.x8) : x; a.lda = c.d;
     a.B = w.ws1; a.ldb = c.d;
     a.M = T; a.N = sm; a.K = c.d;
     a.C = at<void>(ws, p.Hs); a.ldc = sm;
+    if (p.sfp8) { a.b_gscale = w.ws1_scale; a.a_scale = w.shared_act_scale; a.q_scale = w.shared_act_scale + 1; }
     if (p.f32) MOE_TRY(dense_f32(a, false, EPI_SQRELU_F32, h->num_cu, at<float>(ws, p.partial), s));
-    else MOE_TRY(dense_bf16(a, EPI_SQRELU_BF16, h->num_cu, at<float>(ws, p.partial), s));
+    else MOE_TRY(dense_bf16(a, p.sfp8 ? EPI_SQRELU_Q8 : EPI_SQRELU_BF16, h->num_cu,
+                            at<float>(ws, p.partial), s, p.sfp8));
     GemmArgs b = gemm_args();
     b.A = at<void>(ws, p.Hs); b.lda = sm;
     b.B = w.ws2; b.ldb = c.shared_ffn;
     b.kseg = c.shared_ffn; b.b_segstride = (int64_t)c.d * c.shared_ffn;
     b.M = T; b.N = c.d; b.K = sm;
     b.C = at<float>(ws, p.ys); b.ldc = c.d;
+    if (p.sfp8) { b.b_gscale = w.ws2_scale; b.a_scale = w.shared_act_scale + 1; }
     if (p.f32) MOE_TRY(dense_f32(b, false, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
-    else MOE_TRY(dense_bf16(b, EPI_F32, h->num_cu, at<float>(ws, p.partial), s));
+    else MOE_TRY(dense_bf16(b, EPI_F32, h->num_cu, at<float>(ws, p.partial), s, p.sfp8));
     ys = at<float>(ws, p.ys);
   }
   if (c.has_latent_proj) {

@@ -43,10 +43,11 @@ class DeviceLayer:
                         ffn=cfg.ffn, n_shared=cfg.n_shared, shared_ffn=cfg.shared_ffn,
                         max_tokens=self.max_tokens, has_latent_proj=int(cfg.has_latent_proj),
                         act_dtype=B.DTYPES[cfg.act], expert_dtype=B.DTYPES[cfg.expert],
-                        router_on_x=int(cfg.router_on_x))
+                        router_on_x=int(cfg.router_on_x), shared_fp8=int(cfg.shared_fp8))
         w = B.MoEWeights()
         for name in ("w_down", "w_router", "b_router", "w1", "w2", "w1_scale", "w2_scale",
-                     "w1_gscale", "w2_gscale", "w_up", "ws1", "ws2"):
+                     "w1_gscale", "w2_gscale", "w_up", "ws1", "ws2", "act_scale", "ws1_scale",
+                     "ws2_scale", "shared_act_scale"):
             setattr(w, name, _ptr(tensors.get(name)))
         self._c, self._w = c, w
         _, self.handle = B.moe_init(c, w)
@@ -76,14 +77,24 @@ class DeviceLayer:
         put("w_up", wl.w_up(), cfg.act)
         put("w_router", wl.w_router(), "f32")
         put("b_router", wl.b_router(), "f32")
-        put("ws1", wl.ws1(), cfg.act)
-        put("ws2", wl.ws2(), cfg.act)
+        if cfg.shared_fp8 and cfg.n_shared:
+            for name, (codes, sc) in (("ws1", wl.ws1()), ("ws2", wl.ws2())):
+                put(name, codes, "u8")
+                put(name + "_scale", np.array([sc], dtype=np.float32), "f32")
+            put("shared_act_scale", wl.shared_act_scales(), "f32")
+        else:
+            put("ws1", wl.ws1(), cfg.act)
+            put("ws2", wl.ws2(), cfg.act)
+        put("act_scale", wl.act_scales(), "f32")
         N, m, l = cfg.n_experts, cfg.ffn, cfg.latent
         for which, (rows, cols) in (("w1", (m, l)), ("w2", (l, m))):
             fn = wl.w1 if which == "w1" else wl.w2
             if cfg.expert == "nvfp4":
                 codes = torch.empty((N, rows, cols // 2), dtype=torch.uint8, device=dev)
                 scales = torch.empty((N, rows, cols // 16), dtype=torch.uint8, device=dev)
+                gs = np.zeros(N, dtype=np.float32)
+            elif cfg.expert == "fp8":
+                codes = torch.empty((N, rows, cols), dtype=torch.uint8, device=dev)
                 gs = np.zeros(N, dtype=np.float32)
             else:
                 tdt = torch.bfloat16 if cfg.expert == "bf16" else torch.float32
@@ -94,11 +105,17 @@ class DeviceLayer:
                         codes[e].copy_(torch.from_numpy(part[0]))
                         scales[e].copy_(torch.from_numpy(part[1]))
                         gs[e] = part[2]
+                    elif cfg.expert == "fp8":
+                        codes[e].copy_(torch.from_numpy(part[0]))
+                        gs[e] = part[1]
                     else:
                         full[e].copy_(host_tensor(part, cfg.expert))
             if cfg.expert == "nvfp4":
                 t[which] = codes
                 t[which + "_scale"] = scales
+                t[which + "_gscale"] = torch.from_numpy(gs).to(dev)
+            elif cfg.expert == "fp8":
+                t[which] = codes
                 t[which + "_gscale"] = torch.from_numpy(gs).to(dev)
             else:
                 t[which] = full

@@ -59,9 +59,10 @@ class MoEConfig:
     shared_ffn: int = 0    # shared expert FFN width
     has_latent_proj: bool = True
     act: str = "bf16"      # "f32" | "bf16": x, projections, activations
-    expert: str = "bf16"   # "f32" | "bf16" | "nvfp4": routed expert weights
+    expert: str = "bf16"   # "f32" | "bf16" | "nvfp4" | "fp8": routed expert weights
     zipf_s: float = 0.0    # > 0: Zipf(s) expert-popularity bias in the router
     router_on_x: bool = False  # router reads x at d instead of the latent z
+    shared_fp8: bool = False   # shared expert weights (and their inputs) in FP8 E4M3
     margin: float = 1e-4   # top-K gap required by the margin filter (tests)
     description: str = ""
 
@@ -86,6 +87,8 @@ class MoEConfig:
         el = self.latent * self.ffn
         if self.expert == "nvfp4":
             return 2 * (el / 2 + el / 16 + 4)
+        if self.expert == "fp8":
+            return 2 * (el + 4)
         return 2 * el * (4 if self.expert == "f32" else 2)
 
 
@@ -127,6 +130,19 @@ def _cfg_list():
         MoEConfig("latent_8b_decode_router_x", T=64, d=4096, latent=1024, n_experts=512,
                   top_k=22, ffn=1024, n_shared=2, shared_ffn=1024, router_on_x=True,
                   description="LatentMoE, router and 2 shared experts at d, batch decode"),
+        # FP8 (E4M3) weights and activations: configuration 3's prefill and
+        # configuration 4's decode with FP8 experts, and configuration 5 with an
+        # FP8 shared expert beside its NVFP4 routed experts
+        MoEConfig("latent_8b_prefill_fp8", T=8192, d=4096, latent=1024, n_experts=512,
+                  top_k=22, ffn=1024, expert="fp8", zipf_s=1.1,
+                  description="LatentMoE ablation-like prefill, FP8 experts, Zipf routing"),
+        MoEConfig("latent_ultra_decode_fp8", T=64, d=8192, latent=2048, n_experts=512,
+                  top_k=22, ffn=2048, expert="fp8",
+                  description="LatentMoE Ultra-like batch decode, FP8 experts"),
+        MoEConfig("latent_ultra_prefill_nvfp4_shared_fp8", T=16384, d=8192, latent=2048,
+                  n_experts=512, top_k=22, ffn=2048, expert="nvfp4", n_shared=1,
+                  shared_ffn=2048, shared_fp8=True, zipf_s=1.1,
+                  description="LatentMoE Ultra-like prefill, NVFP4 experts, FP8 shared expert"),
     ]
 
 
@@ -155,7 +171,8 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 # Tensor ids for the seed streams.  Never renumber: stored fixtures depend on them.
 _TID = {"x": 1, "x_redraw": 2, "w_down": 3, "w_router": 4, "b_router": 5, "w1": 6,
-        "w2": 7, "w_up": 8, "ws1": 9, "ws2": 10, "nvfp4_w1": 11, "nvfp4_w2": 12}
+        "w2": 7, "w_up": 8, "ws1": 9, "ws2": 10, "nvfp4_w1": 11, "nvfp4_w2": 12,
+        "fp8_w1": 13, "fp8_w2": 14, "fp8_ws1": 15, "fp8_ws2": 16}
 
 # NVFP4 test weights are drawn directly as codes (no quantiser is needed: the
 # oracle and the kernels both consume the same packed bits).  One random byte
@@ -171,6 +188,22 @@ assert _E2M1_MAG_LUT.size == 128
 # Global scale = _NVFP4_C / sqrt(fan_in) keeps the decoded weights near
 # N(0, 1/fan_in) in spread (element rms of code*scale is about 3.5).
 _NVFP4_C = 0.3
+
+# FP8 (E4M3) test weights are drawn directly as codes too: per element one
+# 16-bit random word; bits 0-6 pick the exponent field through a 128-entry
+# table shaped like a quantised N(0, 100^2) (exponent fields 15..6 with
+# frequencies 1,25,41,29,16,8,4,2,1,1 out of 128), bits 7-9 the mantissa (7
+# becomes 6 under exponent field 15, which would be NaN), bit 10 the sign.
+# The per-matrix weight scale _FP8_C / sqrt(fan_in) gives decoded weights of
+# rms about 1/sqrt(fan_in) (the codes' rms is 106.5).
+_FP8_EXP_LUT = np.repeat(np.array([15, 14, 13, 12, 11, 10, 9, 8, 7, 6], dtype=np.uint8),
+                         np.array([1, 25, 41, 29, 16, 8, 4, 2, 1, 1]))
+assert _FP8_EXP_LUT.size == 128
+_FP8_C = 1.0 / 106.5
+# Static per-tensor activation scales of FP8 layers (a calibration constant
+# each: amax / 448 for an expected amax of 6 for the unit-variance inputs z and
+# x, and 36 for the squared-ReLU hidden activations).
+FP8_ACT_AMAX = (6.0, 36.0)
 
 
 class Workload:
@@ -248,16 +281,22 @@ class Workload:
         rank = self._rng("b_router", 0).permutation(c.n_experts) + 1
         return (-c.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
 
-    def ws1(self) -> Optional[np.ndarray]:
+    def ws1(self):
+        """Shared W1 [S][sf][d] in the act dtype, or (E4M3 codes, scale) with shared_fp8."""
         c = self.cfg
         if c.n_shared == 0:
             return None
+        if c.shared_fp8:
+            return self._fp8("fp8_ws1", (c.n_shared, c.shared_ffn, c.d), c.d, 0)
         return self._store(self._normal("ws1", (c.n_shared, c.shared_ffn, c.d), 1.0 / math.sqrt(c.d), 0), c.act)
 
-    def ws2(self) -> Optional[np.ndarray]:
+    def ws2(self):
+        """Shared W2 [S][d][sf], as ws1."""
         c = self.cfg
         if c.n_shared == 0:
             return None
+        if c.shared_fp8:
+            return self._fp8("fp8_ws2", (c.n_shared, c.d, c.shared_ffn), c.shared_ffn, 0)
         return self._store(self._normal("ws2", (c.n_shared, c.d, c.shared_ffn),
                                         1.0 / math.sqrt(c.shared_ffn), 0), c.act)
 
@@ -276,19 +315,45 @@ class Workload:
         gscale = np.float32(_NVFP4_C / math.sqrt(cols))
         return packed, np.ascontiguousarray(scales), gscale
 
+    def _fp8(self, name: str, shape, fan_in: int, *index):
+        g = self._rng(name, *index)
+        r = g.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        e = _FP8_EXP_LUT[r & 127]
+        m = ((r >> 7) & 7).astype(np.uint8)
+        m = np.where((e == 15) & (m == 7), np.uint8(6), m)
+        code = (((r >> 10) & 1).astype(np.uint8) << 7) | (e << 3) | m
+        return np.ascontiguousarray(code.astype(np.uint8)), np.float32(_FP8_C / math.sqrt(fan_in))
+
     def w1(self, e: int):
-        """Expert e's W1 [m][l]: an array, or (codes, scales, gscale) for NVFP4."""
+        """Expert e's W1 [m][l]: an array, (codes, scales, gscale) for NVFP4, or
+        (E4M3 codes, scale) for FP8."""
         c = self.cfg
         if c.expert == "nvfp4":
             return self._nvfp4("nvfp4_w1", e, c.ffn, c.latent)
+        if c.expert == "fp8":
+            return self._fp8("fp8_w1", (c.ffn, c.latent), c.latent, e)
         return self._store(self._normal("w1", (c.ffn, c.latent), 1.0 / math.sqrt(c.latent), e), c.expert)
 
     def w2(self, e: int):
-        """Expert e's W2 [l][m]: an array, or (codes, scales, gscale) for NVFP4."""
+        """Expert e's W2 [l][m]: as w1."""
         c = self.cfg
         if c.expert == "nvfp4":
             return self._nvfp4("nvfp4_w2", e, c.latent, c.ffn)
+        if c.expert == "fp8":
+            return self._fp8("fp8_w2", (c.latent, c.ffn), c.ffn, e)
         return self._store(self._normal("w2", (c.latent, c.ffn), 1.0 / math.sqrt(c.ffn), e), c.expert)
+
+    def act_scales(self) -> Optional[np.ndarray]:
+        """FP8 experts: the per-tensor scales of the expert inputs z and h."""
+        if self.cfg.expert != "fp8":
+            return None
+        return np.array([a / 448.0 for a in FP8_ACT_AMAX], dtype=np.float32)
+
+    def shared_act_scales(self) -> Optional[np.ndarray]:
+        """FP8 shared experts: the per-tensor scales of x and of their hidden rows."""
+        if not (self.cfg.shared_fp8 and self.cfg.n_shared):
+            return None
+        return np.array([a / 448.0 for a in FP8_ACT_AMAX], dtype=np.float32)
 
     def experts_stacked(self, which: str, threads: int = 8):
         """All experts' W1 or W2 stacked on axis 0 (drawn in parallel threads).
@@ -302,4 +367,6 @@ class Workload:
         if self.cfg.expert == "nvfp4":
             return (np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
                     np.array([p[2] for p in parts], dtype=np.float32))
+        if self.cfg.expert == "fp8":
+            return np.stack([p[0] for p in parts]), np.array([p[1] for p in parts], dtype=np.float32)
         return np.stack(parts)

@@ -15,10 +15,17 @@ class ArrayLayer:
     """A layer whose stored tensors are given as arrays (for pins and invariances)."""
 
     def __init__(self, cfg: MoEConfig, x, w_router, w1, w2, w_down=None, w_up=None,
-                 b_router=None, ws1=None, ws2=None):
+                 b_router=None, ws1=None, ws2=None, act_scales=None, shared_act_scales=None):
         self.cfg = cfg
         self._x, self._wr, self._w1, self._w2 = x, w_router, w1, w2
         self._wd, self._wu, self._br, self._ws1, self._ws2 = w_down, w_up, b_router, ws1, ws2
+        self._as, self._sas = act_scales, shared_act_scales
+
+    def act_scales(self):
+        return self._as
+
+    def shared_act_scales(self):
+        return self._sas
 
     def x(self):
         return self._x

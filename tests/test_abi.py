@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -78,6 +78,23 @@ def _good_w(**kw):
     (dict(latent=96), {}, B.MOE_ERR_UNSUPPORTED),                  # not a multiple of 64
     (dict(act_dtype=B.MOE_F32, expert_dtype=B.MOE_BF16), {}, B.MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=B.MOE_BF16, expert_dtype=B.MOE_F32), {}, B.MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=4), {}, B.MOE_ERR_INVALID_ARG),
+    # FP8 experts: per-matrix weight scales and the two activation scales
+    (dict(latent=256, ffn=256, expert_dtype=B.MOE_FP8), {}, B.MOE_ERR_INVALID_ARG),
+    (dict(latent=256, ffn=256, expert_dtype=B.MOE_FP8),
+     dict(w1_gscale=FAKE, w2_gscale=FAKE, act_scale=FAKE + 2), B.MOE_ERR_INVALID_ARG),  # misaligned
+    (dict(latent=64, expert_dtype=B.MOE_FP8),
+     dict(w1_gscale=FAKE, w2_gscale=FAKE, act_scale=FAKE), B.MOE_ERR_UNSUPPORTED),      # l < 256
+    (dict(latent=256, ffn=192, expert_dtype=B.MOE_FP8),
+     dict(w1_gscale=FAKE, w2_gscale=FAKE, act_scale=FAKE), B.MOE_ERR_UNSUPPORTED),      # m % 128
+    (dict(act_dtype=B.MOE_F32, expert_dtype=B.MOE_FP8), {}, B.MOE_ERR_UNSUPPORTED),
+    # FP8 shared experts
+    (dict(shared_fp8=1), {}, B.MOE_ERR_INVALID_ARG),                                 # no shared experts
+    (dict(shared_fp8=2, n_shared=1, shared_ffn=256), dict(ws1=FAKE, ws2=FAKE), B.MOE_ERR_INVALID_ARG),
+    (dict(shared_fp8=1, n_shared=1, shared_ffn=256), dict(ws1=FAKE, ws2=FAKE), B.MOE_ERR_INVALID_ARG),
+    (dict(shared_fp8=1, n_shared=1, shared_ffn=192),
+     dict(ws1=FAKE, ws2=FAKE, ws1_scale=FAKE, ws2_scale=FAKE, shared_act_scale=FAKE),
+     B.MOE_ERR_UNSUPPORTED),                                                          # sf % 128
 ])
 def test_init_rejects_bad_arguments(lib, cfg_kw, w_kw, expect):
     st, h = B.moe_init(_good_cfg(**cfg_kw), _good_w(**w_kw), check=False)
@@ -97,6 +114,16 @@ def test_init_without_device_reports_no_device(lib):
     st, h = B.moe_init(_good_cfg(), _good_w(), check=False)
     assert st == B.MOE_ERR_NO_DEVICE
     assert not h.value
+
+
+def test_quantize_fp8_argument_checks(lib):
+    assert lib.moe_quantize_fp8(FAKE, 0, FAKE, FAKE, None) == B.MOE_OK       # nothing to do
+    assert lib.moe_quantize_fp8(FAKE, 15, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(FAKE, -16, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(None, 16, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(FAKE, 16, None, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(FAKE + 8, 16, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(FAKE, 16, FAKE + 1, FAKE, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_calls_on_null_handle(lib):

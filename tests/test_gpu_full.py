@@ -15,7 +15,7 @@ SAMPLE = 48
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13])
 def test_full_size_config(cfg_id):
     cfg = CONFIGS[cfg_id]
     log("full config %d %s: preparing" % (cfg_id, cfg.name))

@@ -2,8 +2,9 @@
 
 Bar: expert index sets and per-expert counts bit-exact; gates within 1e-5
 (fp32 router and softmax against fp64); y within max|err|/max|ref| of 2e-2
-(bf16), 5e-2 (NVFP4 weights, oracle on the same decoded weights) and 1e-4 for
-the all-fp32 layer.  Routing inputs are margin-filtered (no near-ties at the
+(bf16), 5e-2 (NVFP4 weights, oracle on the same decoded weights), 2e-2 (FP8
+weights and activations, oracle quantising the same way) and 1e-4 for the
+all-fp32 layer.  Routing inputs are margin-filtered (no near-ties at the
 K/K+1 boundary), as the layer configurations ask.
 """
 import sys
@@ -19,7 +20,7 @@ from sparse_moe_layer_fwd_amd.workloads import CONFIGS, MoEConfig, Workload
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "nvfp4": 5e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "nvfp4": 5e-2, "fp8": 2e-2}
 GATE_TOL = 1e-5
 
 
