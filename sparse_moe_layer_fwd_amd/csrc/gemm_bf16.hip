@@ -37,6 +37,8 @@
 // MFMA blocks.  The MFMA computes C^T (weights as the A operand, activations as
 // the B operand) so each lane holds 4 consecutive output columns of one row;
 // bf16 outputs are transposed through LDS before they are stored.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -554,7 +556,9 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 }
 
 // One block's share of one tile list (items first, first + step, ... of the
-// nrt x ntn items), bf16 or NVFP4 weights.  The direct-to-LDS ring runs continuously
+// nrt x ntn items) with NVFP4 weights (bf16 and FP8 operands run
+// gemm_stream_lean: the same ring, waits and barriers with a leaner fragment
+// pipeline, which NVFP4's raw B fragments do not fit).  The direct-to-LDS ring runs continuously
 // across the block's items: the last k-iterations of one item already load the
 // first k-tiles of the next, so its epilogue overlaps those loads and the
 // pipeline never drains between items.  LDS reads are software-pipelined: the
@@ -661,67 +665,83 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
   bar_lds();   // every wave is done with the LDS before the caller reuses it
 }
 
-// FP8 operands of step s (64 codes) for MFMA row block i (A) / column block j
-// (B) of this wavefront (see read_frags).
-template <class C, int WGN>
-__device__ __forceinline__ i32x8 read_a8(const char* stage, int s, int i) {
+// Operands of step s for MFMA row block i (A) or column block j (B) of this
+// wavefront (see read_frags): one 16-byte chunk per lane for bf16 (16-wide
+// step), two for FP8 (64-code step).
+template <class C>
+using LeanOp = typename std::conditional<C::IS_FP8, i32x8, bf16x8>::type;
+template <class C>
+__device__ __forceinline__ LeanOp<C> lean_read(const uint4* rows, int r, int s) {
   constexpr int CPR = C::CPR;
-  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / WGN;
-  const int row = wm * C::WM + i * 32 + (lane & 31), c0 = s * 4 + (lane >> 5);
-  return lds_pair(reinterpret_cast<const uint4*>(stage) + row * CPR, swz_chunk<CPR>(row, c0),
-                  swz_chunk<CPR>(row, c0 + 2));
+  const int h = (threadIdx.x & 63) >> 5;
+  if constexpr (C::IS_FP8) {
+    const int c0 = s * 4 + h;
+    return lds_pair(rows + r * CPR, swz_chunk<CPR>(r, c0), swz_chunk<CPR>(r, c0 + 2));
+  } else {
+    return __builtin_bit_cast(bf16x8, rows[r * CPR + swz_chunk<CPR>(r, s * 2 + h)]);
+  }
 }
 template <class C, int WGN>
-__device__ __forceinline__ i32x8 read_b8(const char* stage, int s, int j) {
-  constexpr int CPR = C::CPR;
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WGN;
-  const int n = wn * C::WN + j * 32 + (lane & 31), c0 = s * 4 + (lane >> 5);
-  return lds_pair(reinterpret_cast<const uint4*>(stage + C::A_BYTES) + n * CPR, swz_chunk<CPR>(n, c0),
-                  swz_chunk<CPR>(n, c0 + 2));
+__device__ __forceinline__ LeanOp<C> lean_a(const char* stage, int s, int i) {
+  const int wm = (threadIdx.x >> 6) / WGN;
+  return lean_read<C>(reinterpret_cast<const uint4*>(stage), wm * C::WM + i * 32 + (threadIdx.x & 31), s);
+}
+template <class C, int WGN>
+__device__ __forceinline__ LeanOp<C> lean_b(const char* stage, int s, int j) {
+  const int wn = (threadIdx.x >> 6) % WGN;
+  return lean_read<C>(reinterpret_cast<const uint4*>(stage + C::A_BYTES), wn * C::WN + j * 32 + (threadIdx.x & 31), s);
+}
+template <class C>
+__device__ __forceinline__ f32x16 lean_mfma(const LeanOp<C>& b, const LeanOp<C>& a, const f32x16& c) {
+  if constexpr (C::IS_FP8)   // E4M3 x E4M3 (format selectors 0), no block scales: the unscaled MFMA
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
 }
 
-// Scheduling order of one FP8 step: per row block I, its TN MFMAs, then its
-// reads (two ds_read_b128 per operand: A block I and the B blocks j = I mod TM).
-template <class C, int I>
-__device__ __forceinline__ void sched_fp8_rows() {
+// Scheduling order of one step: per row block I, its TN MFMAs, then its reads
+// (A block I and the B blocks j = I mod TM; R ds_read_b128 per operand).
+template <class C, int I, int R>
+__device__ __forceinline__ void sched_lean_rows() {
   if constexpr (I < C::TM) {
     constexpr int NB = (C::TN - I + C::TM - 1) / C::TM;
     __builtin_amdgcn_sched_group_barrier(0x008, C::TN, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (1 + NB), 0);
-    sched_fp8_rows<C, I + 1>();
+    __builtin_amdgcn_sched_group_barrier(0x100, R * (1 + NB), 0);
+    sched_lean_rows<C, I + 1, R>();
   }
 }
 
-// One FP8 step: the MFMAs of (fa, fb) and, interleaved with them, the reads of
-// the step after it (step sn of `next`): each A fragment is re-read into its
-// own registers right after its last MFMA (row blocks outermost), B into the
-// other buffer fbn.  One A set plus two B sets keep the 8-wavefront 256x256
-// tile within 256 registers per lane.
+// One step: the MFMAs of (fa, fb) and, interleaved with them, the reads of the
+// step after it (step sn of `next`): each A fragment is re-read into its own
+// registers right after its last MFMA (row blocks outermost), B into the other
+// buffer fbn.  One A set plus two B sets keep the 8-wavefront 256x256 tile
+// within 256 registers per lane.
 template <class C, int WGN>
-__device__ __forceinline__ void step_fp8(f32x16 (&acc)[C::TN][C::TM], i32x8 (&fa)[C::TM],
-                                         const i32x8 (&fb)[C::TN], i32x8 (&fbn)[C::TN],
-                                         const char* next, int sn) {
+__device__ __forceinline__ void lean_step(f32x16 (&acc)[C::TN][C::TM], LeanOp<C> (&fa)[C::TM],
+                                          const LeanOp<C> (&fb)[C::TN], LeanOp<C> (&fbn)[C::TN],
+                                          const char* next, int sn) {
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[j][i], 0, 0, 0, 0, 0, 0);
-    fa[i] = read_a8<C, WGN>(next, sn, i);
+    for (int j = 0; j < C::TN; ++j) acc[j][i] = lean_mfma<C>(fb[j], fa[i], acc[j][i]);
+    fa[i] = lean_a<C, WGN>(next, sn, i);
 #pragma unroll
-    for (int j = i; j < C::TN; j += C::TM) fbn[j] = read_b8<C, WGN>(next, sn, j);
+    for (int j = i; j < C::TN; j += C::TM) fbn[j] = lean_b<C, WGN>(next, sn, j);
   }
-  sched_fp8_rows<C, 0>();
+  sched_lean_rows<C, 0, C::IS_FP8 ? 2 : 1>();
 }
 
-// gemm_stream for FP8 operands (two 64-code steps per k-tile, BK = 64 16-bit
-// slots): the same continuous ring, waits and barrier placement, with the
-// register-lean fragment pipeline of step_fp8.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
-__device__ __forceinline__ void gemm_stream_fp8(const GemmArgs& p, char* smem, const int4* list,
-                                                int nrt, int first, int step) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT_FP8>;
-  constexpr int TM = C::TM, TN = C::TN;
-  static_assert(BK == 64, "two 64-code steps per k-tile");
+// gemm_stream with the register-lean fragment pipeline of lean_step, for bf16
+// and FP8 operands (S steps per k-tile): the same continuous ring, waits and
+// barrier placement.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
+__device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, const int4* list,
+                                                 int nrt, int first, int step) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  using Op = LeanOp<C>;
+  constexpr int TM = C::TM, TN = C::TN, S = C::IS_FP8 ? BK / 32 : BK / 16;
+  static_assert(!C::IS_FP4, "NVFP4 uses gemm_stream");
+  static_assert(S % 2 == 0, "step 0 of every k-tile reads the first B set");
   const int ntn = (p.N + BN - 1) / BN;
   const int total = nrt * ntn;
   if (first >= total) return;
@@ -733,18 +753,18 @@ __device__ __forceinline__ void gemm_stream_fp8(const GemmArgs& p, char* smem, c
   {
     int g, r0, r1, n0;
     item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
-    make_src<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, g, r0, r1, n0, cur);
+    make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, g, r0, r1, n0, cur);
   }
 #pragma unroll
-  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, cur, s, smem + s * C::STAGE);
+  for (int s = 0; s < NST; ++s) issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, s, smem + s * C::STAGE);
   int issued = NST;
   wait_tiles<C::LOADS, NST - 1>(issued - 1);
   bar();
-  i32x8 fa[TM], fb0[TN], fb1[TN];
+  Op fa[TM], fb0[TN], fb1[TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[i] = read_a8<C, WGN>(smem, 0, i);
+  for (int i = 0; i < TM; ++i) fa[i] = lean_a<C, WGN>(smem, 0, i);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) fb0[j] = read_b8<C, WGN>(smem, 0, j);
+  for (int j = 0; j < TN; ++j) fb0[j] = lean_b<C, WGN>(smem, 0, j);
   int gt = 0;
   constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
   int st_tile = -1;
@@ -765,28 +785,32 @@ __device__ __forceinline__ void gemm_stream_fp8(const GemmArgs& p, char* smem, c
     for (int kt = 0; kt < nk; ++kt) {
       const int sg = gt % NST;
       char* st = smem + sg * C::STAGE;
-      step_fp8<C, WGN>(acc, fa, fb0, fb1, st, 1);        // step 0; reads step 1
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s) {                  // steps 0 .. S-2 read steps 1 .. S-1
+        if (s % 2 == 0) lean_step<C, WGN>(acc, fa, fb0, fb1, st, s + 1);
+        else lean_step<C, WGN>(acc, fa, fb1, fb0, st, s + 1);
+      }
       if (kt + 1 < nk || has_next) {
         wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
         bar_lds();
         const int j = kt + NST;
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, cur, j, st);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, j, st);
           ++issued;
         } else if (has_next) {
-          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8>(p, nxt, j - nk, st);
+          if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, nxt, j - nk, st);
           ++issued;
         }
       }
-      // step 1; reads step 0 of the next k-tile (after the last k-tile of the
-      // last item they read a stale stage and are not used)
-      step_fp8<C, WGN>(acc, fa, fb1, fb0, smem + ((gt + 1) % NST) * C::STAGE, 0);
+      // the last step reads step 0 of the next k-tile (after the last k-tile
+      // of the last item they read a stale stage and are not used)
+      lean_step<C, WGN>(acc, fa, fb1, fb0, smem + ((gt + 1) % NST) * C::STAGE, 0);
       ++gt;
     }
     st_tile = issued - 1;
-    epilogue_tile<BM, BN, BK, WGM, WGN, NST, WT_FP8, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
-                                                          smem + NST * C::STAGE, acc);
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, WT, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0,
+                                                      smem + NST * C::STAGE, acc);
     if (!has_next) break;
     cur = nxt;
     it = itn;
@@ -808,10 +832,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   const int G = gridDim.x;
   const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
-  if constexpr (WT == WT_FP8) {
-    gemm_stream_fp8<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
+  if constexpr (WT != WT_NVFP4) {
+    gemm_stream_lean<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
-      gemm_stream_fp8<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+      gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
   } else {
     gemm_stream<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
