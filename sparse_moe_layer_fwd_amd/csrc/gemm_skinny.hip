@@ -30,19 +30,24 @@ __device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
 }  // namespace
 
 // Rows [row0, row0 + cnt) (cnt <= 64) of expert e, columns [n0, n0 + 64).
-// K range [kbeg, kbeg + klen) (klen a multiple of 256): each wavefront takes a
-// quarter.
-template <int WT, int EPI>
+// K range [kbeg, kbeg + klen) (klen a multiple of 256, of 512 when WIDE): each
+// wavefront takes a quarter.  A lane takes 8 * NCH consecutive elements of its
+// rows per step: 16, or 32 E4M3 codes when WIDE (FP8 only), so an FP8 step
+// loads as many bytes per lane as a bf16 one.
+template <int WT, int EPI, bool WIDE = false>
 __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[16][4][64], int e,
                                              int row0, int cnt, int n0, int kbeg, int klen) {
   constexpr bool FP4 = WT == WT_NVFP4, FP8 = WT == WT_FP8;
+  static_assert(!WIDE || FP8, "32-element steps for FP8 codes");
+  constexpr int NCH = WIDE ? 4 : 2;                      // 8-element chunks per lane and step
+  constexpr int KS = 32 * NCH;                           // k per step (4 lane groups)
   constexpr int AEL = FP8 ? 1 : 2;                       // activation element bytes
   constexpr int MAXRB = 4;
   const int nrb = (cnt + 15) >> 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = klen >> 2;
   const int kw0 = kbeg + wave * kq;
-  const int grp = lane >> 4;                             // which 16-wide k slice of a 64-step
+  const int grp = lane >> 4;                             // which k slice of a step
   const char* arow[MAXRB];
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
@@ -79,9 +84,10 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 2
-  for (int kb = kw0; kb < kw0 + kq; kb += 64) {
-    const int k = kb + grp * 16;
-    uint4 b[4][2];
+  for (int kb = kw0; kb < kw0 + kq; kb += KS) {
+    const int k = kb + grp * 8 * NCH;
+    uint4 b[4][NCH];
+    uint4 braw[4][WIDE ? NCH / 2 : 1];                   // WIDE: E4M3 codes, decoded at their MFMAs
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       if (FP4) {
@@ -91,6 +97,9 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
                               fp4x2_bf((c.x >> 16) & 0xFFu, s), fp4x2_bf(c.x >> 24, s));
         b[cb][1] = make_uint4(fp4x2_bf(c.y & 0xFFu, s), fp4x2_bf((c.y >> 8) & 0xFFu, s),
                               fp4x2_bf((c.y >> 16) & 0xFFu, s), fp4x2_bf(c.y >> 24, s));
+      } else if (FP8 && WIDE) {
+#pragma unroll
+        for (int h = 0; h < NCH / 2; ++h) braw[cb][h] = *reinterpret_cast<const uint4*>(brow[cb] + k + 16 * h);
       } else if (FP8) {
         const uint4 c = *reinterpret_cast<const uint4*>(brow[cb] + k);
         b[cb][0] = e4m3x8_bf(c.x, c.y);
@@ -104,25 +113,37 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 #pragma unroll
     for (int rb = 0; rb < MAXRB; ++rb) {
       if (rb < nrb) {
-        uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
+        uint4 a[NCH];
+#pragma unroll
+        for (int h = 0; h < NCH; ++h) a[h] = make_uint4(0, 0, 0, 0);
         if (arow[rb]) {
           const uint4* q = reinterpret_cast<const uint4*>(arow[rb] + k * AEL);
           if (FP8) {
-            const uint4 c = q[0];
-            a0 = e4m3x8_bf(c.x, c.y);
-            a1 = e4m3x8_bf(c.z, c.w);
+#pragma unroll
+            for (int h = 0; h < NCH / 2; ++h) {
+              const uint4 c = q[h];
+              a[2 * h] = e4m3x8_bf(c.x, c.y);
+              a[2 * h + 1] = e4m3x8_bf(c.z, c.w);
+            }
           } else {
-            a0 = q[0];
-            a1 = q[1];
+            a[0] = q[0];
+            a[1] = q[1];
           }
         }
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b[cb][0]), acc[rb][cb], 0, 0, 0);
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b[cb][1]), acc[rb][cb], 0, 0, 0);
-        }
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int h = 0; h < NCH; ++h) {
+            uint4 bh;
+            if constexpr (WIDE) {
+              const uint4 c = braw[cb][h / 2];
+              bh = (h & 1) ? e4m3x8_bf(c.z, c.w) : e4m3x8_bf(c.x, c.y);
+            } else {
+              bh = b[cb][h];
+            }
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[h]), __builtin_bit_cast(bf16x8, bh), acc[rb][cb], 0, 0, 0);
+          }
       }
     }
   }
@@ -181,7 +202,7 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 // Grid (column tiles of 64, experts).  An expert with 0 < count < max_rows is
 // processed in chunks of up to 64 rows; larger experts are left to the tiled
 // GEMM.
-template <int WT, int EPI>
+template <int WT, int EPI, bool WIDE = false>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   __shared__ float red[3][16][4][64];                    // partial sums of waves 1..3
   const int e = blockIdx.y;
@@ -189,7 +210,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   if (cnt == 0 || cnt >= p.max_rows) return;
   const int row0 = p.offs[e];
   for (int c0 = 0; c0 < cnt; c0 += 64) {
-    skinny_chunk<WT, EPI>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
+    skinny_chunk<WT, EPI, WIDE>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
     __syncthreads();
   }
 }
@@ -197,13 +218,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 // Dense split-K: grid (N / 64, ks, row chunks of 64).  Block (x, y, z) sums
 // rows [64 z, 64 z + 64) x columns [64 x, 64 x + 64) over K slice y into the
 // fp32 partials P[y].
-template <int WT>
+template <int WT, bool WIDE = false>
 __global__ __launch_bounds__(256) void skinny_dense_kernel(SkinnyArgs p, int M) {
   __shared__ float red[3][16][4][64];
   const int kl = p.K / (int)gridDim.y;
   const int row0 = blockIdx.z * 64;
-  skinny_chunk<WT, EPI_PARTIAL>(p, red, 0, row0, min(64, M - row0), blockIdx.x * 64,
-                                (int)blockIdx.y * kl, kl);
+  skinny_chunk<WT, EPI_PARTIAL, WIDE>(p, red, 0, row0, min(64, M - row0), blockIdx.x * 64,
+                                      (int)blockIdx.y * kl, kl);
 }
 
 hipError_t launch_skinny_splitk(const GemmArgs& a, bool fp8, int epi, int ks, float* P, hipStream_t s) {
@@ -215,8 +236,9 @@ hipError_t launch_skinny_splitk(const GemmArgs& a, bool fp8, int epi, int ks, fl
   k.N = a.N; k.K = a.K;
   k.P = P; k.p_slice = (int64_t)a.M * a.N;
   dim3 g(a.N / 64, ks, (a.M + 63) / 64), b(256);
-  if (fp8) hipLaunchKernelGGL(skinny_dense_kernel<WT_FP8>, g, b, 0, s, k, a.M);
-  else hipLaunchKernelGGL(skinny_dense_kernel<WT_BF16>, g, b, 0, s, k, a.M);
+  if (fp8 && (a.K / ks) % 512 == 0) hipLaunchKernelGGL((skinny_dense_kernel<WT_FP8, true>), g, b, 0, s, k, a.M);
+  else if (fp8) hipLaunchKernelGGL((skinny_dense_kernel<WT_FP8, false>), g, b, 0, s, k, a.M);
+  else hipLaunchKernelGGL((skinny_dense_kernel<WT_BF16, false>), g, b, 0, s, k, a.M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(a, epi, ks, P, s);
@@ -229,8 +251,11 @@ hipError_t launch_skinny(const SkinnyArgs& a, int wt, int epi, int n_experts, hi
     else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_NVFP4, EPI_BF16>), g, b, 0, s, a);
     else return hipErrorInvalidValue;
   } else if (wt == WT_FP8) {
-    if (epi == EPI_SQRELU_Q8) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_SQRELU_Q8>), g, b, 0, s, a);
-    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_BF16>), g, b, 0, s, a);
+    const bool wide = a.K % 512 == 0;    // 32 codes per lane and step
+    if (epi == EPI_SQRELU_Q8 && wide) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_SQRELU_Q8, true>), g, b, 0, s, a);
+    else if (epi == EPI_SQRELU_Q8) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_SQRELU_Q8, false>), g, b, 0, s, a);
+    else if (epi == EPI_BF16 && wide) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_BF16, true>), g, b, 0, s, a);
+    else if (epi == EPI_BF16) hipLaunchKernelGGL((skinny_kernel<WT_FP8, EPI_BF16, false>), g, b, 0, s, a);
     else return hipErrorInvalidValue;
   } else if (wt == WT_BF16) {
     if (epi == EPI_SQRELU_BF16) hipLaunchKernelGGL((skinny_kernel<WT_BF16, EPI_SQRELU_BF16>), g, b, 0, s, a);

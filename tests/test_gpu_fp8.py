@@ -73,6 +73,10 @@ FP8_SMALL = {
     "fp8_decode_router_on_x": MoEConfig("fp8_decode_router_on_x", T=40, d=512, latent=256,
                                         n_experts=16, top_k=4, ffn=256, expert="fp8",
                                         router_on_x=True),
+    # reductions of 512 and 1024 codes: 32 codes per lane and step in decode
+    "fp8_decode_wide_shared": MoEConfig("fp8_decode_wide_shared", T=24, d=1024, latent=512,
+                                        n_experts=16, top_k=3, ffn=1024, expert="fp8",
+                                        n_shared=1, shared_ffn=512, shared_fp8=True),
     "fp8_multi_item": MoEConfig("fp8_multi_item", T=8192, d=256, latent=256, n_experts=8,
                                 top_k=4, ffn=1024, expert="fp8", zipf_s=1.1),
 }
