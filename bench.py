@@ -20,6 +20,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +107,63 @@ def cpu_baseline(cfg, seed, sample):
                       "fp64 numpy incl. per-expert weight decode; %.2f s" % (sample, cfg.T, seed, dt)}
 
 
+class GpuTelemetry:
+    """Samples the GPU's graphics clock (MHz) and socket power (W) through
+    amdsmi every `period` seconds on a host thread while steps run.  Any
+    failure (no amdsmi, no permission) leaves the record empty."""
+
+    def __init__(self, period=0.02):
+        self.period, self.clk, self.pwr = period, [], []
+        self._stop = threading.Event()
+        self._t = None
+        self.error = None
+
+    def _loop(self, smi, h):
+        while not self._stop.is_set():
+            try:
+                c = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)
+                self.clk.append(float(c["clk"]))
+                pw = smi.amdsmi_get_power_info(h)
+                v = pw.get("current_socket_power", "N/A")
+                if v in ("N/A", None):
+                    v = pw.get("average_socket_power", "N/A")
+                if v not in ("N/A", None):
+                    self.pwr.append(float(v))
+            except Exception as e:      # keep timing, report why the record is empty
+                self.error = repr(e)
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        try:
+            import amdsmi as smi
+            smi.amdsmi_init()
+            h = smi.amdsmi_get_processor_handles()[0]
+        except Exception as e:
+            self.error = repr(e)
+            return self
+        self._t = threading.Thread(target=self._loop, args=(smi, h), daemon=True)
+        self._t.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join()
+        return self
+
+    def record(self):
+        r = {"samples": len(self.clk), "period_s": self.period}
+        if self.clk:
+            r.update({"sclk_mhz_mean": round(sum(self.clk) / len(self.clk), 1), "sclk_mhz_min": min(self.clk),
+                      "sclk_mhz_max": max(self.clk)})
+        if self.pwr:
+            r.update({"power_w_mean": round(sum(self.pwr) / len(self.pwr), 1), "power_w_max": max(self.pwr)})
+        if self.error:
+            r["error"] = self.error
+        return r
+
+
 def time_layer(cfg, cfg_id, seed, steps, warmup):
     """Build the layer with seeded weights, warm up, then time `steps`
     back-to-back moe_forward calls on the current stream (inputs resident in
@@ -146,10 +204,19 @@ def time_layer(cfg, cfg_id, seed, steps, warmup):
     stages = B.moe_profile_read()
     ms_step = start.elapsed_time(end) / steps
     log("bench: %.3f ms/step" % ms_step)
+    # clock and power under the same load: sampled over further steps (at
+    # least 0.5 s) after the timed region, which stays untouched
+    n_tel = max(steps, int(500.0 / max(ms_step, 1e-3)) + 1)
+    tel = GpuTelemetry(period=0.01).start()
+    for _ in range(n_tel):
+        layer.forward(x, ws=ws, y=y)
+    torch.cuda.synchronize()
+    tel.stop()
+    telemetry = dict(tel.record(), steps=n_tel)
     del layer, ws, x, y
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
-            "touched": int((counts_np > 0).sum())}
+            "touched": int((counts_np > 0).sum()), "telemetry": telemetry}
 
 
 # Paired comparisons: (metric, (role a, role b), [(regime, config of a, config of b)])
@@ -310,6 +377,9 @@ def main():
         # decode-regime figure
         "layer_hbm_frac": round(layer_bytes(cfg, touched) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in stages.items() if v[0]},
+        # graphics clock and socket power, sampled over further steps of the
+        # same workload right after the timed region
+        "gpu_telemetry": r["telemetry"],
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
