@@ -280,8 +280,9 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
   }
 }
 
-// Direct-to-LDS loads of k-tile kt of a tile into one stage.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
+// Direct-to-LDS loads of k-tile kt of a tile into one stage: the A part
+// (PARTS bit 0) and the B part (bit 1).
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int PARTS = 3>
 __device__ __forceinline__ void issue_tile(const GemmArgs& p,
                                            const TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& s,
                                            int kt, char* stage) {
@@ -290,12 +291,16 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
   constexpr int NW = C::NW;
   const int wave = threadIdx.x >> 6;
   const uint32_t k0 = (uint32_t)kt * BK;
+  if constexpr (PARTS & 1) {
 #pragma unroll
-  for (int j = 0; j < C::A_PW; ++j) {
-    const int blk = (wave + j * NW) % C::A_TOT;
-    dma16(s.A + (s.aoff[j] + k0), stage + blk * 1024);
+    for (int j = 0; j < C::A_PW; ++j) {
+      const int blk = (wave + j * NW) % C::A_TOT;
+      dma16(s.A + (s.aoff[j] + k0), stage + blk * 1024);
+    }
   }
-  if (FP4) {
+  if constexpr (!(PARTS & 2)) {
+    return;
+  } else if (FP4) {
 #pragma unroll
     for (int j = 0; j < C::B_PW; ++j) {
       const int blk = (wave + j * NW) % C::B_TOT;
@@ -790,22 +795,30 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
         if (s % 2 == 0) lean_step<C, WGN>(acc, fa, fb0, fb1, st, s + 1);
         else lean_step<C, WGN>(acc, fa, fb1, fb0, st, s + 1);
       }
+      // refill stage sg with the k-tile NST ahead: its A part right after the
+      // barrier, its B part after the tile's last step, so that the 8
+      // wavefronts' loads do not all queue at the address unit at once
+      const int j = kt + NST;
+      int refill = 0;                    // 1: k-tile j of this item, 2: k-tile j - nk of the next
       if (kt + 1 < nk || has_next) {
         wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
         bar_lds();
-        const int j = kt + NST;
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, j, st);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, j, st);
+          refill = 1;
           ++issued;
         } else if (has_next) {
           if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, nxt, j - nk, st);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, nxt, j - nk, st);
+          refill = 2;
           ++issued;
         }
       }
       // the last step reads step 0 of the next k-tile (after the last k-tile
       // of the last item they read a stale stage and are not used)
       lean_step<C, WGN>(acc, fa, fb1, fb0, smem + ((gt + 1) % NST) * C::STAGE, 0);
+      if (refill == 1) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, j, st);
+      else if (refill == 2) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, nxt, j - nk, st);
       ++gt;
     }
     st_tile = issued - 1;
