@@ -440,25 +440,8 @@ __device__ __forceinline__ void epilogue_tile(
   }
 }
 
-// Operand fragments of one k substep for one wavefront: 16 bf16 wide, or 64
-// E4M3 codes wide (FP8: each lane's 16 bytes of two consecutive 16-wide bf16
-// substeps).  NVFP4 B fragments stay raw (8 codes and their block scale) until
-// the MFMAs use them.
-template <class C, int W = (C::IS_FP4 ? WT_NVFP4 : C::IS_FP8 ? WT_FP8 : WT_BF16)>
-struct Frags {
-  bf16x8 a[C::TM], b[C::TN];
-};
-template <class C>
-struct Frags<C, WT_NVFP4> {
-  bf16x8 a[C::TM];
-  uint32_t bq[C::TN], bs[C::TN];
-};
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-template <class C>
-struct Frags<C, WT_FP8> {
-  i32x8 a[C::TM], b[C::TN];                      // one MFMA operand each (32 codes)
-};
 // two 16-byte LDS chunks -> one 8-dword MFMA operand
 __device__ __forceinline__ i32x8 lds_pair(const uint4* base, int c0, int c1) {
   const i32x4 lo = *reinterpret_cast<const i32x4*>(base + c0);
@@ -466,80 +449,54 @@ __device__ __forceinline__ i32x8 lds_pair(const uint4* base, int c0, int c1) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// NVFP4 pipeline: operand fragments of one 16-wide k substep for one
+// wavefront.  The B fragments stay raw (8 codes and their block scale) until
+// the MFMAs use them.
+template <class C>
+struct Fp4Frags {
+  bf16x8 a[C::TM];
+  uint32_t bq[C::TN], bs[C::TN];
+};
+
 // Fragments of substep s of the k-tile in `stage`.  kbyte: position of the
-// k-tile's first scale byte in the aligned scale dword of each row (NVFP4).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
-__device__ __forceinline__ void read_frags(const char* stage, int s, int kbyte,
-                                           Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& f) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+// k-tile's first scale byte in the aligned scale dword of each row.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST>
+__device__ __forceinline__ void read_fp4_frags(const char* stage, int s, int kbyte,
+                                               Fp4Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>>& f) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>;
   constexpr int CPR = C::CPR, WM = C::WM, WN = C::WN;
   const uint4* As = reinterpret_cast<const uint4*>(stage);
-  const uint4* Bs = reinterpret_cast<const uint4*>(stage + C::A_BYTES);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  if constexpr (C::IS_FP8) {
-    // step s: 16-byte chunks 4s + h and 4s + 2 + h for lane half h
-    const int c0 = s * 4 + (lane >> 5);
+  const int ch = s * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int row = wm * WM + i * 32 + (lane & 31);
-      f.a[i] = lds_pair(As + row * CPR, swz_chunk<CPR>(row, c0), swz_chunk<CPR>(row, c0 + 2));
-    }
+  for (int i = 0; i < C::TM; ++i) {
+    const int row = wm * WM + i * 32 + (lane & 31);
+    f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
+  }
+  // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
+  // 8(s & 1) + 4h of 32-k chunk s / 2
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
+  const uint8_t* Sc = Q + C::BQ_BYTES;
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = wn * WN + j * 32 + (lane & 31);
-      f.b[j] = lds_pair(Bs + n * CPR, swz_chunk<CPR>(n, c0), swz_chunk<CPR>(n, c0 + 2));
-    }
-  } else {
-    const int ch = s * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int row = wm * WM + i * 32 + (lane & 31);
-      f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
-    }
-    if constexpr (C::FP4) {
-      // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
-      // 8(s & 1) + 4h of 32-k chunk s / 2
-      const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
-      const uint8_t* Sc = Q + C::BQ_BYTES;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int n = wn * WN + j * 32 + (lane & 31);
-        f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
-                                                     ((lane >> 5) << 2));
-        f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int n = wn * WN + j * 32 + (lane & 31);
-        f.b[j] = __builtin_bit_cast(bf16x8, Bs[n * CPR + swz_chunk<CPR>(n, ch)]);
-      }
-    }
+  for (int j = 0; j < C::TN; ++j) {
+    const int n = wn * WN + j * 32 + (lane & 31);
+    f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
+                                                 ((lane >> 5) << 2));
+    f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
   }
 }
 
-// acc += fragments (the MFMA computes C^T: weights as its A operand).  NVFP4
-// B fragments are decoded here, exactly, to bf16.
+// acc += fragments (the MFMA computes C^T: weights as its A operand); the B
+// fragments are decoded here, exactly, to bf16.
 template <class C>
-__device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
-  if constexpr (C::IS_FP8) {
+__device__ __forceinline__ void mma_fp4_frags(const Fp4Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+  for (int j = 0; j < C::TN; ++j) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        // E4M3 x E4M3 (format selectors 0), no block scales: the unscaled MFMA
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[j][i], 0, 0, 0, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      bf16x8 b;
-      if constexpr (C::IS_FP4) b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
-      else b = f.b[j];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
-    }
+    for (int i = 0; i < C::TM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
   }
 }
 
@@ -548,8 +505,7 @@ __device__ __forceinline__ void mma_frags(const Frags<C>& f, f32x16 (&acc)[C::TN
 // instead of stalling the wavefront before the first of them.
 template <class C>
 __device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int NR = C::IS_FP8 ? 2 * (C::TM + C::TN) : C::TM + (C::IS_FP4 ? 2 : 1) * C::TN;
-  constexpr int NM = C::TM * C::TN;
+  constexpr int NR = C::TM + 2 * C::TN, NM = C::TM * C::TN;
   constexpr int P = NR < NM ? NR : NM;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
@@ -576,11 +532,12 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 // after them is needed.  NVFP4 stages hold the raw codes and scales; each
 // wavefront decodes the B fragments it multiplies (those of its wavefront
 // column), so the decode runs on the VALU beside the other wavefront's MFMAs.
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
-__device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const int4* list,
-                                            int nrt, int first, int step) {
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
+__device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, const int4* list,
+                                                int nrt, int first, int step) {
+  constexpr int WT = WT_NVFP4;
   using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
-  constexpr int TM = C::TM, TN = C::TN, S = C::IS_FP8 ? BK / 32 : BK / 16;
+  constexpr int TM = C::TM, TN = C::TN, S = BK / 16;
   static_assert(S % 2 == 0, "substep 0 of every k-tile uses the first register set");
   const int ntn = (p.N + BN - 1) / BN;
   const int total = nrt * ntn;
@@ -600,10 +557,10 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
   int issued = NST;          // k-tiles of this stream issued so far
   wait_tiles<C::LOADS, NST - 1>(issued - 1);
   bar();
-  Frags<C> f0, f1;
+  Fp4Frags<C> f0, f1;
   // the aligned scale dword of each row holds k-tile kt's first scale at this byte
   auto kbyte = [](int kt) { return (kt * (BK / 16)) & 3; };
-  read_frags<BM, BN, BK, WGM, WGN, NST, WT>(smem, 0, 0, f0);
+  read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(smem, 0, 0, f0);
   int gt = 0;                // k-tiles of this stream consumed so far
   // stores per thread of one staged epilogue (all issued, see epilogue_tile)
   constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
@@ -628,11 +585,11 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
         if (s % 2 == 0) {
-          read_frags<BM, BN, BK, WGM, WGN, NST, WT>(st, s + 1, kbyte(kt), f1);
-          mma_frags<C>(f0, acc);
+          read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, kbyte(kt), f1);
+          mma_fp4_frags<C>(f0, acc);
         } else {
-          read_frags<BM, BN, BK, WGM, WGN, NST, WT>(st, s + 1, kbyte(kt), f0);
-          mma_frags<C>(f1, acc);
+          read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, kbyte(kt), f0);
+          mma_fp4_frags<C>(f1, acc);
         }
         interleave_reads_mfma<C>();
       }
@@ -651,12 +608,12 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
           issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, nxt, j - nk, fs);
           ++issued;
         }
-        read_frags<BM, BN, BK, WGM, WGN, NST, WT>(smem + ((gt + 1) % NST) * C::STAGE, 0,
+        read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(smem + ((gt + 1) % NST) * C::STAGE, 0,
                                                    kbyte(kt + 1 < nk ? kt + 1 : 0), f0);
       }
       // one call site for the last substep: duplicating it in both branches
       // doubles the live accumulators and spills them
-      mma_frags<C>(f1, acc);
+      mma_fp4_frags<C>(f1, acc);
       interleave_reads_mfma<C>();
       ++gt;
     }
@@ -671,7 +628,7 @@ __device__ __forceinline__ void gemm_stream(const GemmArgs& p, char* smem, const
 }
 
 // Operands of step s for MFMA row block i (A) or column block j (B) of this
-// wavefront (see read_frags): one 16-byte chunk per lane for bf16 (16-wide
+// wavefront: swizzled LDS chunks as in the direct-to-LDS ring; one 16-byte chunk per lane for bf16 (16-wide
 // step), two for FP8 (64-code step).
 template <class C>
 using LeanOp = typename std::conditional<C::IS_FP8, i32x8, bf16x8>::type;
@@ -736,7 +693,7 @@ __device__ __forceinline__ void lean_step(f32x16 (&acc)[C::TN][C::TM], LeanOp<C>
   sched_lean_rows<C, 0, C::IS_FP8 ? 2 : 1>();
 }
 
-// gemm_stream with the register-lean fragment pipeline of lean_step, for bf16
+// gemm_stream_fp4's ring with the register-lean fragment pipeline of lean_step, for bf16
 // and FP8 operands (S steps per k-tile): the same continuous ring, waits and
 // barrier placement.
 template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
@@ -745,7 +702,7 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
   using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
   using Op = LeanOp<C>;
   constexpr int TM = C::TM, TN = C::TN, S = C::IS_FP8 ? BK / 32 : BK / 16;
-  static_assert(!C::IS_FP4, "NVFP4 uses gemm_stream");
+  static_assert(!C::IS_FP4, "NVFP4 uses gemm_stream_fp4");
   static_assert(S % 2 == 0, "step 0 of every k-tile reads the first B set");
   const int ntn = (p.N + BN - 1) / BN;
   const int total = nrt * ntn;
@@ -795,24 +752,27 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
         if (s % 2 == 0) lean_step<C, WGN>(acc, fa, fb0, fb1, st, s + 1);
         else lean_step<C, WGN>(acc, fa, fb1, fb0, st, s + 1);
       }
-      // refill stage sg with the k-tile NST ahead: its A part right after the
-      // barrier, its B part after the tile's last step, so that the 8
-      // wavefronts' loads do not all queue at the address unit at once
+      // refill stage sg with the k-tile NST ahead.  With 8 wavefronts its A
+      // part goes out right after the barrier and its B part after the tile's
+      // last step, so that their 64 loads do not all queue at the address
+      // unit at once; with 4 the whole k-tile goes out after the barrier.
+      constexpr int FIRST = C::NW == 8 ? 1 : 3;
       const int j = kt + NST;
       int refill = 0;                    // 1: k-tile j of this item, 2: k-tile j - nk of the next
       if (kt + 1 < nk || has_next) {
         wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
         bar_lds();
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, j, st);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, FIRST>(p, cur, j, st);
           refill = 1;
           ++issued;
         } else if (has_next) {
           if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, nxt, j - nk, st);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, FIRST>(p, nxt, j - nk, st);
           refill = 2;
           ++issued;
         }
+        if (FIRST == 3) refill = 0;
       }
       // the last step reads step 0 of the next k-tile (after the last k-tile
       // of the last item they read a stale stage and are not used)
@@ -850,9 +810,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
     if constexpr (BMS > 0)
       gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
   } else {
-    gemm_stream<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
+    gemm_stream_fp4<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
-      gemm_stream<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+      gemm_stream_fp4<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
   }
 }
 
