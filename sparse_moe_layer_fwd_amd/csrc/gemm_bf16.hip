@@ -593,21 +593,28 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
         }
         interleave_reads_mfma<C>();
       }
+      // refill stage sg with the k-tile NST ahead (with 8 wavefronts: A part
+      // after the barrier, codes and scales after the last substep)
+      constexpr int FIRST = C::NW == 8 ? 1 : 3;
+      const int j = kt + NST;
+      char* fs = smem + sg * C::STAGE;
+      int refill = 0;                    // 1: k-tile j of this item, 2: k-tile j - nk of the next
       if (kt + 1 < nk || has_next) {
         // k-tile gt + 1 landed (own loads), own reads of stage sg complete;
         // after the barrier the same holds for every wavefront
         wait_tile<C::LOADS, NST - 2, ST>(gt + 1, issued, st_tile);
         bar_lds();
-        const int j = kt + NST;          // refill stage sg with the k-tile NST ahead
-        char* fs = smem + sg * C::STAGE;
         if (j < nk) {
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, cur, j, fs);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, FIRST>(p, cur, j, fs);
+          refill = 1;
           ++issued;
         } else if (has_next) {
           if (j == nk) make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt);
-          issue_tile<BM, BN, BK, WGM, WGN, NST, WT>(p, nxt, j - nk, fs);
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, FIRST>(p, nxt, j - nk, fs);
+          refill = 2;
           ++issued;
         }
+        if (FIRST == 3) refill = 0;
         read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(smem + ((gt + 1) % NST) * C::STAGE, 0,
                                                    kbyte(kt + 1 < nk ? kt + 1 : 0), f0);
       }
@@ -615,6 +622,8 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
       // doubles the live accumulators and spills them
       mma_fp4_frags<C>(f1, acc);
       interleave_reads_mfma<C>();
+      if (refill == 1) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, j, fs);
+      else if (refill == 2) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, nxt, j - nk, fs);
       ++gt;
     }
     st_tile = issued - 1;
