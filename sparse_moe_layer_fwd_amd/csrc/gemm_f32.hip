@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     // split-K (EPI_PARTIAL): slice blockIdx.y of gridDim.y covers K / gridDim.y
     const int kl = EPI == EPI_PARTIAL ? p.K / (int)gridDim.y : p.K;
     const int kb = EPI == EPI_PARTIAL ? (int)blockIdx.y * kl : 0;
-    for (int k0 = kb; k0 < kb + kl; k0 += BK) {
-      float av[8], bv[8];
+    // this thread's 8 A and 8 B values of k-step k0, loaded one k-step ahead
+    // (registers) so that their latency overlaps the MFMAs of the current one
+    auto load = [&](int k0, float (&av)[8], float (&bv)[8]) {
       if (ABF16) {
         const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)p.A + arow * p.lda + k0 + kq);
         av[0] = bf2f(v.x & 0xFFFFu); av[1] = bf2f(v.x >> 16);
@@ -57,17 +58,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         av[0] = x0.x; av[1] = x0.y; av[2] = x0.z; av[3] = x0.w;
         av[4] = x1.x; av[5] = x1.y; av[6] = x1.z; av[7] = x1.w;
       }
-      {
-        const int seg = k0 / p.kseg, kin = k0 - seg * p.kseg;
-        const float4* q = reinterpret_cast<const float4*>(Bg + (int64_t)seg * p.b_segstride + kin + kq);
-        const float4 x0 = q[0], x1 = q[1];
-        bv[0] = x0.x; bv[1] = x0.y; bv[2] = x0.z; bv[3] = x0.w;
-        bv[4] = x1.x; bv[5] = x1.y; bv[6] = x1.z; bv[7] = x1.w;
-      }
-      __syncthreads();
+      const int seg = k0 / p.kseg, kin = k0 - seg * p.kseg;
+      const float4* q = reinterpret_cast<const float4*>(Bg + (int64_t)seg * p.b_segstride + kin + kq);
+      const float4 x0 = q[0], x1 = q[1];
+      bv[0] = x0.x; bv[1] = x0.y; bv[2] = x0.z; bv[3] = x0.w;
+      bv[4] = x1.x; bv[5] = x1.y; bv[6] = x1.z; bv[7] = x1.w;
+    };
+    float av[8], bv[8];
+    load(kb, av, bv);
+    for (int k0 = kb; k0 < kb + kl; k0 += BK) {
+      __syncthreads();                                   // the previous k-step's reads are done
 #pragma unroll
       for (int i = 0; i < 8; ++i) { As[lr][kq + i] = av[i]; Bs[lr][kq + i] = bv[i]; }
       __syncthreads();
+      if (k0 + BK < kb + kl) load(k0 + BK, av, bv);
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 4) {
         float a[2], b[2];
