@@ -35,7 +35,9 @@
  *   - Errors are integer status codes; every argument check runs on the host
  *     before any launch, so a failing call enqueues nothing.
  *   - A handle is immutable after moe_init and may be used from several host
- *     threads; concurrent calls need distinct workspaces.
+ *     threads; concurrent calls need distinct workspaces.  It belongs to the
+ *     device that was current at moe_init: moe_route / moe_forward return
+ *     MOE_ERR_INVALID_ARG when another device is current.
  */
 #ifndef MOE_H_
 #define MOE_H_

@@ -37,6 +37,7 @@
 // MFMA blocks.  The MFMA computes C^T (weights as the A operand, activations as
 // the B operand) so each lane holds 4 consecutive output columns of one row;
 // bf16 outputs are transposed through LDS before they are stored.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -837,12 +838,17 @@ hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t 
   auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, WT, EPI>;
   // every stage of the ring holds a k-tile of the first output tile
   if (a.K / BK1 < NST1 || (BMS > 0 && a.K / BK2 < NST2)) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+  // the dynamic-LDS limit, set once per device (idempotent if two host
+  // threads race on the first launch)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   // persistent grid: as many blocks as fit at once (a multiple of the 8 XCDs)
   const int per_cu = (int)((160 * 1024) / lds);

@@ -240,6 +240,9 @@ int check_call(moe_handle_t h, const void* x, int32_t T, void* ws, size_t ws_byt
   if (!h) return MOE_ERR_INVALID_ARG;
   if (T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
+  int dev = -1;                            // the handle's weights live on its device
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev != h->device) return MOE_ERR_INVALID_ARG;
   if (!x || !aligned16(x)) return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(h->c, T, h->num_cu);
   if (!ws || ws_bytes < p.total) return MOE_ERR_WORKSPACE;
