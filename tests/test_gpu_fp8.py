@@ -77,6 +77,9 @@ FP8_SMALL = {
     "fp8_decode_wide_shared": MoEConfig("fp8_decode_wide_shared", T=24, d=1024, latent=512,
                                         n_experts=16, top_k=3, ffn=1024, expert="fp8",
                                         n_shared=1, shared_ffn=512, shared_fp8=True),
+    "fp8_decode_max_experts_max_k": MoEConfig("fp8_decode_max_experts_max_k", T=20, d=256,
+                                              latent=256, n_experts=1024, top_k=64, ffn=256,
+                                              expert="fp8"),
     "fp8_multi_item": MoEConfig("fp8_multi_item", T=8192, d=256, latent=256, n_experts=8,
                                 top_k=4, ffn=1024, expert="fp8", zipf_s=1.1),
 }

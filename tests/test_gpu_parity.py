@@ -126,6 +126,9 @@ SMALL = {
                                 ffn=1024),
     "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
                                   top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
+    # the largest N and K the ABI accepts (top-K over 1024 logits, 64 per token)
+    "max_experts_max_k": MoEConfig("max_experts_max_k", T=130, d=256, latent=128, n_experts=1024,
+                                   top_k=64, ffn=128),
     # routing on x at d (shared experts at d beside latent routed experts)
     "router_on_x_shared": MoEConfig("router_on_x_shared", T=300, d=256, latent=128, n_experts=16,
                                     top_k=4, ffn=128, n_shared=1, shared_ffn=128,
