@@ -192,18 +192,25 @@ def time_layer(cfg, cfg_id, seed, steps, warmup):
 
     stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one more event per step boundary: per-step times for the median
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     B.moe_profile_read()                      # clear
     B.moe_profile_enable(True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(steps):
+    marks[0].record(stream)
+    for i in range(steps):
         layer.forward(x, ws=ws, y=y)
+        marks[i + 1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     B.moe_profile_enable(False)
     stages = B.moe_profile_read()
     ms_step = start.elapsed_time(end) / steps
-    log("bench: %.3f ms/step" % ms_step)
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    step_stats = {"median": round(per_step[len(per_step) // 2], 5), "min": round(per_step[0], 5),
+                  "max": round(per_step[-1], 5)}
+    log("bench: %.3f ms/step (median %.3f)" % (ms_step, step_stats["median"]))
     # clock and power under the same load: sampled over further steps (at
     # least 0.5 s) after the timed region, which stays untouched
     n_tel = max(steps, int(500.0 / max(ms_step, 1e-3)) + 1)
@@ -216,7 +223,7 @@ def time_layer(cfg, cfg_id, seed, steps, warmup):
     del layer, ws, x, y
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
-            "touched": int((counts_np > 0).sum()), "telemetry": telemetry}
+            "touched": int((counts_np > 0).sum()), "telemetry": telemetry, "step_stats": step_stats}
 
 
 # Paired comparisons: (metric, (role a, role b), [(regime, config of a, config of b)])
@@ -361,6 +368,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        # per-step HIP-event times over the same timed steps
+        "ms_per_step_stats": r["step_stats"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
