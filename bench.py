@@ -164,7 +164,7 @@ class GpuTelemetry:
         return r
 
 
-def time_layer(cfg, cfg_id, seed, steps, warmup):
+def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0):
     """Build the layer with seeded weights, warm up, then time `steps`
     back-to-back moe_forward calls on the current stream (inputs resident in
     HBM) with the library's per-stage timer on."""
@@ -212,14 +212,16 @@ def time_layer(cfg, cfg_id, seed, steps, warmup):
                   "max": round(per_step[-1], 5)}
     log("bench: %.3f ms/step (median %.3f)" % (ms_step, step_stats["median"]))
     # clock and power under the same load: sampled over further steps (at
-    # least 0.5 s) after the timed region, which stays untouched
-    n_tel = max(steps, int(500.0 / max(ms_step, 1e-3)) + 1)
-    tel = GpuTelemetry(period=0.01).start()
-    for _ in range(n_tel):
-        layer.forward(x, ws=ws, y=y)
-    torch.cuda.synchronize()
-    tel.stop()
-    telemetry = dict(tel.record(), steps=n_tel)
+    # least telemetry_ms) after the timed region, which stays untouched
+    telemetry = None
+    if telemetry_ms > 0:
+        n_tel = max(steps, int(telemetry_ms / max(ms_step, 1e-3)) + 1)
+        tel = GpuTelemetry(period=0.01).start()
+        for _ in range(n_tel):
+            layer.forward(x, ws=ws, y=y)
+        torch.cuda.synchronize()
+        tel.stop()
+        telemetry = dict(tel.record(), steps=n_tel)
     del layer, ws, x, y
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
@@ -288,6 +290,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--telemetry-ms", type=float, default=500.0,
+                    help="sample clock and power over this many ms of extra steps after the timed "
+                         "region (0: off, e.g. under a profiler)")
     ap.add_argument("--paired", nargs="?", const="ablation", choices=sorted(PAIRS), default=None,
                     help="time a pair of layers instead: 'ablation' (standard vs latent, "
                          "configurations 6/3 and 7/8), 'router_at_d' (3/9 and 8/10) or 'fp8' "
@@ -326,7 +331,7 @@ def main():
         return
 
     cfg = CONFIGS[args.config]
-    r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup)
+    r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup, args.telemetry_ms)
     ms_step, stages, counts_np, touched = r["ms_step"], r["stages"], r["counts"], r["touched"]
 
     # dominant kernel: the grouped expert GEMMs (two launches per step)
