@@ -302,8 +302,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build measures the layer on a single MI355X "
-              "(--gpus %d requested). Multi-GPU expert parallelism is not built." % args.gpus,
+        print("bench.py runs on one GPU only: it measures the layer on a single MI355X "
+              "(--gpus %d requested). Multi-GPU expert parallelism is not implemented." % args.gpus,
               file=sys.stderr, flush=True)
         sys.exit(2)
 
