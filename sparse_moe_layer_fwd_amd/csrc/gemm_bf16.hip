@@ -46,18 +46,33 @@ namespace moe {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
+// Direct-to-LDS loads (M0 = the wavefront's LDS destination, each lane's
+// bytes at M0 + lane * size).  They are written as inline asm so that the
+// compiler's waitcnt insertion does not see them: with an LDS-DMA of its own in
+// flight it waits for every outstanding fragment read (lgkmcnt(0)) at each MFMA
+// step instead of only the ones that step needs.  Their completion is tracked
+// by the explicit vmcnt waits below.  The asm has no register outputs.  M0 is
+// a reserved register: the compiler sets it right before each instruction of
+// its own that reads it (none in these kernels), hence the clobber, and the
+// warning that clobbering a reserved register draws is silenced here.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
 // 4-byte direct load (sub-dword LDS-DMA forms are not used: their LDS placement
 // is not the 2- or 1-byte lane stride the packed layouts here would need)
 template <int BYTES>
 __device__ __forceinline__ void dma_small(const void* g, void* lds_wave_base) {
   static_assert(BYTES == 4, "dword LDS-DMA only");
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
