@@ -25,45 +25,68 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 __device__ __forceinline__ uint32_t key_expert(uint64_t k) {
   return 0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu);
 }
-// One DPP step of a 64-bit max: combine with the value of another lane of the
-// same row (quad permutations and row rotations have no memory round-trip).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
-}
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-// Wave-wide max: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror 4, row_ror 8
-// leave every lane with its 16-lane row's max; the four row maxima are then read
-// as scalars.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0xB1>(v);
-  v = dpp_max_step<0x4E>(v);
-  v = dpp_max_step<0x124>(v);
-  v = dpp_max_step<0x128>(v);
-  const uint64_t a = readlane64(v, 0), b = readlane64(v, 16);
-  const uint64_t c = readlane64(v, 32), d = readlane64(v, 48);
-  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
-  return ab > cd ? ab : cd;
-}
-
 // Zero `n` ints (the chunk histograms) with plain stores: safe inside captured graphs.
 __global__ __launch_bounds__(256) void zero_kernel(int* __restrict__ p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 
-// One wavefront per token (4 per block).  Each lane holds the logits of experts
-// lane, lane+64, ...; K rounds of a wave-wide max over packed (value, id) keys
-// give the K largest in descending order.  The per-chunk expert histogram of
-// chunk t / tc is kept with integer atomics (order-independent results).
+// Wave-wide max of a 32-bit value: the same four DPP steps leave each lane
+// with its row's max, then the four row maxima are combined as scalars.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1>(v);
+  v = dpp_max_u32<0x4E>(v);
+  v = dpp_max_u32<0x124>(v);
+  v = dpp_max_u32<0x128>(v);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
+// a where the lane's bit of `lanes` is clear, b where it is set (one
+// v_cndmask with a scalar lane mask; written out so that the per-round pop
+// below stays a plain shift instead of an indexed select over all keys)
+__device__ __forceinline__ uint32_t sel_lanes(uint32_t a, uint32_t b, uint64_t lanes) {
+  uint32_t d;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(lanes));
+  return d;
+}
+
+// Descending bitonic sorting network over a lane's NJ keys (NJ a power of 2).
+template <int NJ>
+__device__ __forceinline__ void sort_keys_desc(uint64_t (&k)[NJ]) {
+#pragma unroll
+  for (int size = 2; size <= NJ; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t a = k[i], b = k[j];
+          const bool sw = ((i & size) == 0) ? a < b : a > b;
+          k[i] = sw ? b : a;
+          k[j] = sw ? a : b;
+        }
+      }
+}
+
+// One wavefront per token (4 per block).  Each lane holds the keys (value,
+// then lower expert id first; see make_key) of experts lane, lane+64, ...,
+// sorted descending, so its best remaining key is always key[0].  Each of the
+// K rounds takes the wave-wide max of the lanes' best values, breaks a tie in
+// value by the key's id half (a second max, only when several lanes hold the
+// value), and pops the winning lane's key: the K largest keys in descending
+// order.  The per-chunk expert histogram of chunk t / tc is kept with integer
+// atomics (order-independent results).
 template <int NJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int N,
                                                    int K, int tc, int* __restrict__ idx,
@@ -72,23 +95,49 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // all NJ loads go out before any is used (lanes past N re-read the row's
+  // last logit and get the invalid key 0, below every valid key)
+  const float* row = logits + (int64_t)t * N;
+  float lv[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) lv[j] = row[min(j * 64 + lane, N - 1)];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(lv[j]));  // keeps the loads together
   uint64_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = j * 64 + lane;
-    key[j] = e < N ? make_key(logits[(int64_t)t * N + e], (uint32_t)e) : 0ull;
+    key[j] = e < N ? make_key(lv[j], (uint32_t)e) : 0ull;
   }
-  uint32_t taken = 0;
+  sort_keys_desc<NJ>(key);
+  uint32_t khi[NJ], klo[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    khi[j] = (uint32_t)(key[j] >> 32);
+    klo[j] = (uint32_t)key[j];
+  }
   uint64_t mine = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;
-    int bj = -1;
+    const uint32_t hi = khi[0], lo = klo[0];
+    const uint32_t mhi = wave_max_u32(hi);
+    uint64_t at = __ballot(hi == mhi);             // lanes whose best value is the max
+    uint32_t mlo;
+    if (__popcll(at) == 1) {
+      mlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((unsigned long long)at) - 1);
+    } else {                                       // equal values: the larger id half wins
+      mlo = wave_max_u32(hi == mhi ? lo : 0u);
+      at = __ballot(hi == mhi && lo == mlo);
+    }
+    // pop the winning lane's best key (a one-bit lane mask)
+    const uint64_t wm = 1ull << (__ffsll((unsigned long long)at) - 1);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (!((taken >> j) & 1u) && key[j] > best) { best = key[j]; bj = j; }
-    const uint64_t w = wave_max_u64(best);
-    if (bj >= 0 && best == w) taken |= 1u << bj;
-    if (lane == k) mine = w;
+    for (int j = 0; j + 1 < NJ; ++j) {
+      khi[j] = sel_lanes(khi[j], khi[j + 1], wm);
+      klo[j] = sel_lanes(klo[j], klo[j + 1], wm);
+    }
+    khi[NJ - 1] = sel_lanes(khi[NJ - 1], 0u, wm);
+    klo[NJ - 1] = sel_lanes(klo[NJ - 1], 0u, wm);
+    if (lane == k) mine = ((uint64_t)mhi << 32) | mlo;
   }
   const float v = key_value(mine);
   const float vmax = __shfl(v, 0, 64);
@@ -159,12 +208,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   int total = 0;
   if (e < N) {
     int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {            // 8 independent loads in flight
-      int v[8];
+    for (; c + 32 <= nchunks; c += 32) {          // 32 independent loads in flight
+      int v[32];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = chunk_counts[(int64_t)(c + i) * N + e];
+      for (int i = 0; i < 32; ++i) v[i] = chunk_counts[(int64_t)(c + i) * N + e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(v[i]));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
         chunk_base[(int64_t)(c + i) * N + e] = total;
         total += v[i];
       }
@@ -208,10 +259,13 @@ hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int 
   return hipGetLastError();
 }
 
-// One wavefront per chunk of tc tokens.  Tokens are visited in order; lane k
-// handles assignment (t, k).  A token's K experts are distinct, so the K lanes
-// update K different LDS counters: within an expert the slots follow (t, k)
-// order, a stable and deterministic scatter.
+// One wavefront per chunk of tc tokens (tc * K <= kScatterMax).  The chunk's
+// expert ids and its per-expert start slots are first staged in LDS with all
+// loads in flight; then tokens are visited in order, lane k handling
+// assignment (t, k).  A token's K experts are distinct, so the K lanes update
+// K different LDS counters: within an expert the slots follow (t, k) order, a
+// stable and deterministic scatter.
+constexpr int kScatterMax = 2048;
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx, int T, int K,
                                                      int N, int tc,
                                                      const int* __restrict__ chunk_base,
@@ -219,18 +273,44 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx
                                                      int* __restrict__ slot_token,
                                                      int* __restrict__ tk_slot) {
   __shared__ int cnt[1024];
+  __shared__ int sidx[kScatterMax];
   const int c = blockIdx.x, lane = threadIdx.x;
-  for (int i = lane; i < N; i += 64) cnt[i] = offs[i] + chunk_base[(int64_t)c * N + i];
+  const int t0 = c * tc, t1 = min(T, t0 + tc);
+  const int n = (t1 - t0) * K;
+  const int* src = idx + (int64_t)t0 * K;
+  const int* cb = chunk_base + (int64_t)c * N;
+  for (int i0 = 0; i0 < n; i0 += 8 * 64) {        // 8 loads per lane in flight
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * 64 + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * 64 + lane < n) sidx[i0 + u * 64 + lane] = v[u];
+  }
+  for (int i0 = 0; i0 < N; i0 += 8 * 64) {
+    int a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u * 64 + lane, N - 1);
+      a[u] = offs[i];
+      b[u] = cb[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(a[u]), "+v"(b[u]));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * 64 + lane < N) cnt[i0 + u * 64 + lane] = a[u] + b[u];
+  }
   __syncthreads();
-  const int t1 = min(T, (c + 1) * tc);
-  for (int t = c * tc; t < t1; ++t) {
+  for (int t = t0; t < t1; ++t) {
     if (lane < K) {
-      const int64_t a = (int64_t)t * K + lane;
-      const int e = idx[a];
+      const int e = sidx[(t - t0) * K + lane];
       const int slot = cnt[e];
       cnt[e] = slot + 1;
       slot_token[slot] = t;
-      tk_slot[a] = slot;
+      tk_slot[(int64_t)t * K + lane] = slot;
     }
   }
 }
@@ -238,6 +318,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ idx
 hipError_t launch_scatter(const int* idx, int T, int K, int N, int tc, const int* chunk_base,
                           const int* offs, int* slot_token, int* tk_slot, hipStream_t s) {
   const int nchunks = (T + tc - 1) / tc;
+  if ((int64_t)tc * K > kScatterMax || N > 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, idx, T, K, N, tc,
                      chunk_base, offs, slot_token, tk_slot);
   return hipGetLastError();

@@ -180,6 +180,45 @@ def test_degree_two_homogeneity_bitwise():
     assert torch.equal(y2, 4 * y1)
 
 
+class _IntegerRouter(Workload):
+    """Exact logit ties: integer x in [-2, 2] and a router on x whose rows repeat
+    eight integer patterns, so every logit is an integer, exact in fp32 and in
+    fp64, and each value is shared by about N/8 experts.  The tie rule (equal
+    logits: lower expert id first) then decides the order on both sides."""
+
+    def x(self):
+        from sparse_moe_layer_fwd_amd.workloads import f32_to_bf16_bits
+        c = self.cfg
+        v = np.random.default_rng([self.seed, 101]).integers(-2, 3, size=(c.T, c.d)).astype(np.float32)
+        return f32_to_bf16_bits(v)
+
+    def w_router(self):
+        c = self.cfg
+        pat = np.random.default_rng([self.seed, 102]).integers(-1, 2, size=(8, c.d)).astype(np.float32)
+        return np.ascontiguousarray(pat[np.arange(c.n_experts) % 8])
+
+    def b_router(self):
+        return None
+
+
+@pytest.mark.parametrize("n,k", [(40, 6), (300, 22), (1000, 64)])
+def test_exact_logit_ties_take_lower_expert_ids(n, k):
+    cfg = MoEConfig("ties_%d_%d" % (n, k), T=130, d=128, latent=64, n_experts=n, top_k=k,
+                    ffn=128, router_on_x=True)
+    log("case %s" % cfg.name)
+    wl = _IntegerRouter(cfg, 0)
+    dl = DeviceLayer.from_workload(wl)
+    y, idx, gate, counts = dl.forward(x_to_device(wl), routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(wl, cfg)
+    assert np.array_equal(idx.cpu().numpy(), ref.idx), "top-K order differs under exact ties"
+    assert np.array_equal(counts.cpu().numpy(), ref.counts)
+    assert np.max(np.abs(gate.cpu().numpy() - ref.gate)) <= GATE_TOL
+    err = rel_err(y.float().cpu().numpy().astype(np.float64), ref.y)
+    log("  y rel err %.3e" % err)
+    assert err <= TOL["bf16"], err
+
+
 class _UnitScaleFp4(Workload):
     """NVFP4 weights with global scale 1: their decoded values are exact bf16."""
 
