@@ -113,7 +113,118 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
+// Wide tiles for the large dense fp32 GEMMs (the router of a prefill batch):
+// BM x 128 x 32 with BM = 64 or 128, 4 wavefronts in a 2x2 grid, each
+// (BM/2) x 64 as v_mfma_f32_32x32x2_f32 blocks (4 times the MFMA work per
+// fragment read of the 64x64 tile above).  Operands are double-buffered in
+// LDS with one barrier per k-step; the next k-step's global loads sit in
+// registers while the current one is multiplied.  The sums run over k in
+// ascending order within each MFMA chain, as in every other fp32 GEMM here.
+template <bool ABF16, int BM>
+__global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
+  constexpr int BN = 128, BK = 32, LD = BK + 1, TI = BM / 64;
+  __shared__ float As[2][BM * LD];
+  __shared__ float Bs[2][BN * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = p.N / BN;
+  const int total = ((p.M + BM - 1) / BM) * ntn;
+  const int nk = p.K / BK;
+  const int lr = tid >> 3, kc = (tid & 7) * 4;     // rows lr + 32 q, k chunk kc .. kc + 3
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int rt = item / ntn, nt = item - rt * ntn;
+    const int r0 = rt * BM, n0 = nt * BN;
+    f32x4 ra[BM / 32], rb[4];
+    auto load = [&](int k0) {
+#pragma unroll
+      for (int q = 0; q < BM / 32; ++q) {
+        const int64_t row = min(r0 + lr + 32 * q, p.M - 1);
+        if (ABF16) {
+          const uint2 v = *reinterpret_cast<const uint2*>((const uint16_t*)p.A + row * p.lda + k0 + kc);
+          ra[q] = f32x4{bf2f(v.x & 0xFFFFu), bf2f(v.x >> 16), bf2f(v.y & 0xFFFFu), bf2f(v.y >> 16)};
+        } else {
+          ra[q] = *reinterpret_cast<const f32x4*>((const float*)p.A + row * p.lda + k0 + kc);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        rb[q] = *reinterpret_cast<const f32x4*>((const float*)p.B + (int64_t)(n0 + lr + 32 * q) * p.ldb + k0 + kc);
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < BM / 32; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) As[buf][(lr + 32 * q) * LD + kc + i] = ra[q][i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Bs[buf][(lr + 32 * q) * LD + kc + i] = rb[q][i];
+    };
+    f32x16 acc[TI][2];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    __syncthreads();                                     // the previous item's reads are done
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < nk) load((ks + 1) * BK);
+      const float* Ab = As[buf] + (wm * (BM / 2) + (lane & 31)) * LD + (lane >> 5);
+      const float* Bb = Bs[buf] + (wn * 64 + (lane & 31)) * LD + (lane >> 5);
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 2) {
+        float a[TI], b[2];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) a[i] = Ab[i * 32 * LD + kk];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = Bb[j * 32 * LD + kk];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+      if (ks + 1 < nk) store(buf ^ 1);
+      __syncthreads();
+    }
+    // D[m][n] of each 32x32 block: n = lane % 32, m = 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        const float bias = p.bias ? p.bias[col] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < p.M) ((float*)p.C)[(int64_t)row * p.ldc + col] = acc[i][j][r] + bias;
+        }
+      }
+  }
+}
+
 hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_cap, hipStream_t s) {
+  if (!a.tiles && !a.a_rows && epi == EPI_F32 && a.N % 128 == 0 && a.K % 32 == 0 && a.kseg >= a.K &&
+      a.lda % 4 == 0 && a.ldb % 4 == 0) {
+    // grid_cap is two blocks per CU: 128-row tiles when they fill it, else 64-row
+    const int64_t t128 = (int64_t)((a.M + 127) / 128) * (a.N / 128);
+    const int64_t t64 = (int64_t)((a.M + 63) / 64) * (a.N / 128);
+    if (t64 >= grid_cap) {
+      const bool big = t128 >= grid_cap;
+      const int64_t total = big ? t128 : t64;
+      dim3 g((unsigned)(total < grid_cap ? total : grid_cap)), b(256);
+      if (big && a_is_bf16) hipLaunchKernelGGL((gemm_f32_wide_kernel<true, 128>), g, b, 0, s, a);
+      else if (big) hipLaunchKernelGGL((gemm_f32_wide_kernel<false, 128>), g, b, 0, s, a);
+      else if (a_is_bf16) hipLaunchKernelGGL((gemm_f32_wide_kernel<true, 64>), g, b, 0, s, a);
+      else hipLaunchKernelGGL((gemm_f32_wide_kernel<false, 64>), g, b, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int ntn = (a.N + 63) / 64;
   const int nrt_max = a.tiles ? a.M : (a.M + 63) / 64;   // grouped: M carries the tile bound
   int64_t total = (int64_t)nrt_max * ntn;
