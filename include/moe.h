@@ -125,6 +125,8 @@ typedef struct {
  * act F32 requires expert F32; act BF16 requires expert BF16, NVFP4 or FP8.
  * FP8 experts: l and m multiples of 128 and at least 256.  shared_fp8: d and
  * shared_ffn multiples of 128, d and n_shared * shared_ffn at least 256.
+ * Every activation matrix of a call (up to max_tokens * top_k rows) and every
+ * weight matrix must be smaller than 4 GiB (the GEMMs use 32-bit byte offsets).
  * Outside these rules the call returns MOE_ERR_UNSUPPORTED.
  * Returns MOE_ERR_NO_DEVICE when no HIP device is visible. */
 int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out);

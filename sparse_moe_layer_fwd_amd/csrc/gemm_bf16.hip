@@ -60,17 +60,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
-               : "memory", "m0");
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, void* lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 // 4-byte direct load (sub-dword LDS-DMA forms are not used: their LDS placement
 // is not the 2- or 1-byte lane stride the packed layouts here would need)
 template <int BYTES>
-__device__ __forceinline__ void dma_small(const void* g, void* lds_wave_base) {
+__device__ __forceinline__ void dma_small(const char* base, uint32_t off, void* lds_wave_base) {
   static_assert(BYTES == 4, "dword LDS-DMA only");
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds_wave_base))
-               : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+               "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -201,7 +201,7 @@ __device__ __forceinline__ void wait_tile(int need, int issued, int st_tile) {
 template <class C>
 struct TileSrc {
   int g, r0, r1, n0;
-  const uint16_t* A;
+  const char* A;
   const char* B;
   const char* S;
   uint32_t aoff[C::A_PW], boff[C::B_PW], soff[C::S_PW1];
@@ -238,7 +238,7 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   s.g = g; s.r0 = r0; s.r1 = r1; s.n0 = n0;
-  s.A = (const uint16_t*)p.A;
+  s.A = (const char*)p.A;
 #pragma unroll
   for (int j = 0; j < C::A_PW; ++j) {
     const int blk = (wave + j * NW) % C::A_TOT;
@@ -266,10 +266,10 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
     } else {
       pr = (uint32_t)min(r0 + row, r1 - 1);        // rows past the end re-read the last row
     }
-    s.aoff[j] = pr * (uint32_t)p.lda + swz_chunk<CPR>(row, pos) * 8;
+    s.aoff[j] = (pr * (uint32_t)p.lda + swz_chunk<CPR>(row, pos) * 8) * 2;   // bytes
   }
   s.B = FP4 ? (const char*)p.B + (int64_t)g * p.b_gstride
-            : (const char*)((const uint16_t*)p.B + (int64_t)g * p.b_gstride);
+            : (const char*)p.B + (int64_t)g * p.b_gstride * 2;
   s.S = FP4 ? (const char*)p.b_scale + (int64_t)g * p.s_gstride : nullptr;
 #pragma unroll
   for (int j = 0; j < C::B_PW; ++j) {
@@ -284,7 +284,7 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
     } else {
       const int q = blk * 64 + lane, row = q / CPR, pos = q % CPR;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
-      s.boff[j] = n * (uint32_t)p.ldb + swz_chunk<CPR>(row, pos) * 8;   // elements
+      s.boff[j] = (n * (uint32_t)p.ldb + swz_chunk<CPR>(row, pos) * 8) * 2;   // bytes
     }
   }
 #pragma unroll
@@ -311,7 +311,7 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
 #pragma unroll
     for (int j = 0; j < C::A_PW; ++j) {
       const int blk = (wave + j * NW) % C::A_TOT;
-      dma16(s.A + (s.aoff[j] + k0), stage + blk * 1024);
+      dma16(s.A + k0 * 2, s.aoff[j], stage + blk * 1024);
     }
   }
   if constexpr (!(PARTS & 2)) {
@@ -320,23 +320,23 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
 #pragma unroll
     for (int j = 0; j < C::B_PW; ++j) {
       const int blk = (wave + j * NW) % C::B_TOT;
-      dma16(s.B + (s.boff[j] + k0 / 2), stage + C::A_BYTES + blk * 1024);
+      dma16(s.B + k0 / 2, s.boff[j], stage + C::A_BYTES + blk * 1024);
     }
 #pragma unroll
     for (int j = 0; j < C::S_PW; ++j) {
       const int blk = (wave + j * NW) % C::S_TOT1;
-      dma_small<4>(s.S + ((s.soff[j] + k0 / 16) & ~3u), stage + C::A_BYTES + C::BQ_BYTES + blk * 256);
+      dma_small<4>(s.S + ((k0 / 16) & ~3u), s.soff[j], stage + C::A_BYTES + C::BQ_BYTES + blk * 256);
     }
   } else {
-    const uint16_t* Bk = (const uint16_t*)s.B + k0;
+    const char* Bk = s.B + k0 * 2;
     if (p.kseg < p.K) {                    // B stored as k segments (shared experts' W2)
       const int seg = (int)(k0 / (uint32_t)p.kseg);
-      Bk = (const uint16_t*)s.B + (int64_t)seg * p.b_segstride + (k0 - (uint32_t)seg * p.kseg);
+      Bk = s.B + ((int64_t)seg * p.b_segstride + (k0 - (uint32_t)seg * p.kseg)) * 2;
     }
 #pragma unroll
     for (int j = 0; j < C::B_PW; ++j) {
       const int blk = (wave + j * NW) % C::B_TOT;
-      dma16(Bk + s.boff[j], stage + C::A_BYTES + blk * 1024);
+      dma16(Bk, s.boff[j], stage + C::A_BYTES + blk * 1024);
     }
   }
 }

@@ -428,6 +428,19 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
   if (c.shared_fp8 && (c.act_dtype != MOE_BF16 || c.d % 128 || c.shared_ffn % 128 || c.d < 256 ||
                        c.n_shared * c.shared_ffn < 256))
     return MOE_ERR_UNSUPPORTED;
+  // the tiled GEMMs address each operand with 32-bit byte offsets from a
+  // uniform base: every activation matrix (up to max_tokens * top_k rows) and
+  // every weight matrix must stay below 4 GiB
+  {
+    const int64_t lim = (int64_t)1 << 32, es = c.act_dtype == MOE_F32 ? 4 : 2;
+    const int64_t T = c.max_tokens, TK = (int64_t)c.max_tokens * c.top_k;
+    const int64_t sw = (int64_t)c.n_shared * c.shared_ffn;
+    const int64_t wide = std::max<int64_t>(std::max<int64_t>(c.d, c.latent), std::max<int64_t>(c.ffn, sw));
+    if (TK * std::max(c.ffn, c.latent) * es >= lim || T * wide * es >= lim ||
+        (int64_t)c.d * std::max<int64_t>(c.latent, sw) * es >= lim ||
+        (int64_t)c.ffn * c.latent * es >= lim)
+      return MOE_ERR_UNSUPPORTED;
+  }
   // weights
   if (!w->w_router || !aligned16(w->w_router) || !w->w1 || !aligned16(w->w1) || !w->w2 ||
       !aligned16(w->w2))

@@ -95,11 +95,25 @@ def _good_w(**kw):
     (dict(shared_fp8=1, n_shared=1, shared_ffn=192),
      dict(ws1=FAKE, ws2=FAKE, ws1_scale=FAKE, ws2_scale=FAKE, shared_act_scale=FAKE),
      B.MOE_ERR_UNSUPPORTED),                                                          # sf % 128
+    # 32-bit byte offsets: T*K hidden rows of 2048 bf16 reach 4 GiB at T*K = 2^20
+    (dict(d=8192, latent=2048, ffn=2048, n_experts=512, top_k=22, max_tokens=48000), {},
+     B.MOE_ERR_UNSUPPORTED),
+    (dict(d=65536, latent=32768, ffn=128), {}, B.MOE_ERR_UNSUPPORTED),               # W_d = 4 GiB
 ])
 def test_init_rejects_bad_arguments(lib, cfg_kw, w_kw, expect):
     st, h = B.moe_init(_good_cfg(**cfg_kw), _good_w(**w_kw), check=False)
     assert st == expect, B.status_string(st)
     assert not h.value
+
+
+def test_init_accepts_the_largest_offsets_below_4gib(lib):
+    # 47662 tokens * 22 * 2048 * 2 bytes < 2^32: passes the shape rules (then
+    # MOE_ERR_NO_DEVICE without a GPU, a handle with one)
+    st, h = B.moe_init(_good_cfg(d=8192, latent=2048, ffn=2048, n_experts=512, top_k=22,
+                                 max_tokens=47662), _good_w(), check=False)
+    assert st in (B.MOE_OK, B.MOE_ERR_NO_DEVICE), B.status_string(st)
+    if h.value:
+        B.moe_destroy(h)
 
 
 def test_init_null_pointers(lib):
