@@ -60,8 +60,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// a wavefront-uniform pointer, kept in scalar registers for the asm's "s" operand
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, void* lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 // 4-byte direct load (sub-dword LDS-DMA forms are not used: their LDS placement
@@ -69,7 +76,7 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t off, void* lds_
 template <int BYTES>
 __device__ __forceinline__ void dma_small(const char* base, uint32_t off, void* lds_wave_base) {
   static_assert(BYTES == 4, "dword LDS-DMA only");
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
                "s"(lds_addr(lds_wave_base)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -777,11 +784,12 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
         if (s % 2 == 0) lean_step<C, WGN>(acc, fa, fb0, fb1, st, s + 1);
         else lean_step<C, WGN>(acc, fa, fb1, fb0, st, s + 1);
       }
-      // refill stage sg with the k-tile NST ahead.  With 8 wavefronts its A
-      // part goes out right after the barrier and its B part after the tile's
-      // last step, so that their 64 loads do not all queue at the address
-      // unit at once; with 4 the whole k-tile goes out after the barrier.
-      constexpr int FIRST = C::NW == 8 ? 1 : 3;
+      // refill stage sg with the k-tile NST ahead.  With 8 wavefronts its B
+      // part (the weights, the loads that cost the most) goes out right after
+      // the barrier and its A part after the tile's last step, so that their 64
+      // loads do not all queue at the address unit at once; with 4 the whole
+      // k-tile goes out after the barrier.
+      constexpr int FIRST = C::NW == 8 ? 2 : 3;
       const int j = kt + NST;
       int refill = 0;                    // 1: k-tile j of this item, 2: k-tile j - nk of the next
       if (kt + 1 < nk || has_next) {
@@ -802,8 +810,8 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
       // the last step reads step 0 of the next k-tile (after the last k-tile
       // of the last item they read a stale stage and are not used)
       lean_step<C, WGN>(acc, fa, fb1, fb0, smem + ((gt + 1) % NST) * C::STAGE, 0);
-      if (refill == 1) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, j, st);
-      else if (refill == 2) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, nxt, j - nk, st);
+      if (refill == 1) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, j, st);
+      else if (refill == 2) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, nxt, j - nk, st);
       ++gt;
     }
     st_tile = issued - 1;
