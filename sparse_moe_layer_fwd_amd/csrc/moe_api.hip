@@ -73,8 +73,11 @@ int prof_begin(int stage, hipStream_t s) {
   std::lock_guard<std::mutex> g(P.mu);
   if (!P.on) return -1;
   hipEvent_t a = prof_event(), b = prof_event();
-  if (!a || !b) return -1;
-  hipEventRecord(a, s);
+  if (!a || !b || hipEventRecord(a, s) != hipSuccess) {   // no record for this stage
+    if (a) P.pool.push_back(a);
+    if (b) P.pool.push_back(b);
+    return -1;
+  }
   P.pending.push_back({stage, a, b});
   return (int)P.pending.size() - 1;
 }
@@ -82,7 +85,8 @@ void prof_end(int rec, hipStream_t s) {
   if (rec < 0) return;
   Prof& P = prof();
   std::lock_guard<std::mutex> g(P.mu);
-  if (rec < (int)P.pending.size()) hipEventRecord(P.pending[rec].b, s);
+  // a failed end record surfaces as a failed elapsed-time query in moe_profile_read
+  if (rec < (int)P.pending.size()) (void)hipEventRecord(P.pending[rec].b, s);
 }
 struct StageScope {
   int rec;
