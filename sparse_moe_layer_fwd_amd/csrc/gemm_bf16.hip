@@ -25,7 +25,9 @@
 // Data movement: operands go global -> LDS with gfx950's direct-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane)
 // through a ring of NST stages, so NST-1 k-tiles are in flight while one is
-// multiplied and no VGPRs are spent on staging.  The ring runs continuously
+// multiplied and no VGPRs are spent on staging.  The grouped 8-wavefront
+// bf16 / FP8 kernels split the ring by operand instead: 2 A stages and 3 B
+// (weight) stages in the same LDS, the weights loaded one k-tile further ahead.  The ring runs continuously
 // over each persistent block's sequence of output tiles.  Each wavefront waits for its
 // own loads with an explicit vmcnt, then a bare s_barrier publishes the stage.
 // LDS rows hold BK bf16 as 16-byte chunks; chunk c of row r sits at c ^ f(r),
@@ -725,6 +727,158 @@ __device__ __forceinline__ void lean_step(f32x16 (&acc)[C::TN][C::TM], LeanOp<C>
   sched_lean_rows<C, 0, C::IS_FP8 ? 2 : 1>();
 }
 
+// lean_step with the A and B operands in separate stages (b_stage - A_BYTES is
+// passed as the B side's "stage" so that lean_b's offset lands in b_stage)
+template <class C, int WGN>
+__device__ __forceinline__ void lean_step_ab(f32x16 (&acc)[C::TN][C::TM], LeanOp<C> (&fa)[C::TM],
+                                             const LeanOp<C> (&fb)[C::TN], LeanOp<C> (&fbn)[C::TN],
+                                             const char* anext, const char* bnext, int sn) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j][i] = lean_mfma<C>(fb[j], fa[i], acc[j][i]);
+    fa[i] = lean_a<C, WGN>(anext, sn, i);
+#pragma unroll
+    for (int j = i; j < C::TN; j += C::TM) fbn[j] = lean_b<C, WGN>(bnext - C::A_BYTES, sn, j);
+  }
+  sched_lean_rows<C, 0, C::IS_FP8 ? 2 : 1>();
+}
+
+// 8-wavefront bf16 / FP8 tiles: the same continuous fragment pipeline with
+// separate rings for the operands, 2 A stages and 3 B stages (the weights,
+// whose loads cost the most, are issued a k-tile earlier).  Per k-tile: after
+// the wait for k-tile gt + 1 and the barrier, A k-tile gt + 2 refills the A
+// stage just consumed; after the tile's last step B k-tile gt + 3 refills its
+// B stage.  Each wait then leaves exactly the newest B group (and, after an
+// item's epilogue, its stores) in flight.  The epilogue stages its rows in the
+// B stage just consumed and issues that stage's refill after it.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int EPI>
+__device__ __forceinline__ void gemm_stream_ab(const GemmArgs& p, char* smem, const int4* list,
+                                               int nrt, int first, int step) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
+  using Op = LeanOp<C>;
+  constexpr int TM = C::TM, TN = C::TN, S = C::IS_FP8 ? BK / 32 : BK / 16;
+  constexpr int NA = 2, NB = 3;
+  static_assert(!C::IS_FP4 && C::NW == 8, "8-wavefront bf16 / FP8 tiles");
+  static_assert(S % 2 == 0, "step 0 of every k-tile reads the first B set");
+  static_assert(EpiKind<EPI>::STAGED ? 32 * WGM * BN * EpiKind<EPI>::ELEM <= C::B_BYTES : true,
+                "epilogue staging fits a B stage");
+  static_assert(C::A_PW + C::B_PW < 64 && 2 * C::B_PW + C::A_PW < 64, "vmcnt range");
+  const int ntn = (p.N + BN - 1) / BN;
+  const int total = nrt * ntn;
+  if (first >= total) return;
+  const int nk = p.K / BK;                           // >= NB (checked by the launcher)
+  char* const abase = smem;
+  char* const bbase = smem + NA * C::A_BYTES;
+  auto astage = [&](int t) { return abase + (t % NA) * C::A_BYTES; };
+  auto bstage = [&](int t) { return bbase + (t % NB) * C::B_BYTES; };   // the B data itself
+  constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
+
+  wait_vm<0>();
+  TileSrc<C> cur, nxt;
+  int it = first;
+  {
+    int g, r0, r1, n0;
+    item_coords<BM, BN>(p, list, nrt, ntn, it, g, r0, r1, n0);
+    make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, g, r0, r1, n0, cur);
+  }
+  // prologue, in this order: A0 B0 B1 A1 B2
+  issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, 0, astage(0));
+  issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, 0, bstage(0) - C::A_BYTES);
+  issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, 1, bstage(1) - C::A_BYTES);
+  issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, 1, astage(1));
+  issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, 2, bstage(2) - C::A_BYTES);
+  wait_vm<2 * C::B_PW + C::A_PW>();                  // A0 and B0 landed
+  bar();
+  Op fa[TM], fb0[TN], fb1[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[i] = lean_a<C, WGN>(astage(0), 0, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb0[j] = lean_b<C, WGN>(bstage(0) - C::A_BYTES, 0, j);
+  int gt = 0;
+  // in flight after the newest A group: 1 = one B group, 2 = one B group and
+  // an epilogue's stores
+  int after_a = 1;
+
+  for (;;) {
+    const int itn = it + step;
+    const bool has_next = itn < total;
+    int ng = 0, nr0 = 0, nr1 = 0, nn0 = 0;
+    if (has_next) item_coords<BM, BN>(p, list, nrt, ntn, itn, ng, nr0, nr1, nn0);
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+    bool made_nxt = false;
+    int bdelay = -1;                                 // B k-tile (of nxt) left for after the epilogue
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* as = astage(gt);
+      const char* bs = bstage(gt);
+#pragma unroll
+      for (int s = 0; s + 1 < S; ++s) {              // steps 0 .. S-2 read steps 1 .. S-1
+        if (s % 2 == 0) lean_step_ab<C, WGN>(acc, fa, fb0, fb1, as, bs, s + 1);
+        else lean_step_ab<C, WGN>(acc, fa, fb1, fb0, as, bs, s + 1);
+      }
+      const bool more = kt + 1 < nk || has_next;     // a k-tile gt + 1 exists
+      if (more) {
+        // A and B of k-tile gt + 1 landed (own loads), own reads of this
+        // tile's stages complete; after the barrier the same holds for all
+        if (after_a == 2) wait_vm<C::B_PW + ST>();
+        else if (after_a == 1) wait_vm<C::B_PW>();
+        else wait_vm<0>();
+        bar_lds();
+        // A k-tile gt + 2 into the A stage just consumed
+        const int ja = kt + NA;
+        if (ja < nk) {
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, ja, astage(gt));
+        } else if (has_next) {
+          if (!made_nxt) { make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt); made_nxt = true; }
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, nxt, ja - nk, astage(gt));
+        }
+      }
+      // the last step reads step 0 of k-tile gt + 1 (stale stages after the
+      // last k-tile of the last item: read, not used)
+      lean_step_ab<C, WGN>(acc, fa, fb1, fb0, astage(gt + 1), bstage(gt + 1), 0);
+      // B k-tile gt + 3 into the B stage just consumed; an item's last k-tile
+      // keeps that stage for the epilogue and issues the load after it
+      const int jb = kt + NB;
+      after_a = 0;
+      if (more) {
+        if (jb < nk) {
+          issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, cur, jb, bstage(gt) - C::A_BYTES);
+          after_a = 1;
+        } else if (has_next) {
+          if (!made_nxt) { make_src<BM, BN, BK, WGM, WGN, NST, WT>(p, ng, nr0, nr1, nn0, nxt); made_nxt = true; }
+          if (kt + 1 < nk) {
+            issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, nxt, jb - nk, bstage(gt) - C::A_BYTES);
+            after_a = 1;
+          } else {
+            bdelay = jb - nk;
+          }
+        }
+      }
+      ++gt;
+    }
+    // epilogue in the B stage of the item's last k-tile (gt - 1), free since
+    // that k-tile's barrier (the last item's last k-tile has none: add it)
+    if (!has_next) bar_lds();
+    char* est = bstage(gt - 1);
+    epilogue_tile<BM, BN, BK, WGM, WGN, NST, WT, EPI>(p, cur.g, cur.r0, cur.r1, cur.n0, est, acc);
+    if (!has_next) break;
+    if (bdelay >= 0) {
+      issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 2>(p, nxt, bdelay, est - C::A_BYTES);
+      after_a = 2;
+    }
+    cur = nxt;
+    it = itn;
+  }
+  bar_lds();
+}
+
 // gemm_stream_fp4's ring with the register-lean fragment pipeline of lean_step, for bf16
 // and FP8 operands (S steps per k-tile): the same continuous ring, waits and
 // barrier placement.
@@ -838,7 +992,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   const int G = gridDim.x;
   const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
-  if constexpr (WT != WT_NVFP4) {
+  if constexpr (WT != WT_NVFP4 && WGM * WGN == 8 && BK1 == 64 && BK2 == 64 && BMS > 0) {
+    if (p.K >= 3 * BK1) {                    // three B stages of one tile
+      gemm_stream_ab<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
+      if constexpr (BMS > 0)
+        gemm_stream_ab<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+    } else {
+      gemm_stream_lean<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
+      if constexpr (BMS > 0)
+        gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+    }
+  } else if constexpr (WT != WT_NVFP4) {
     gemm_stream_lean<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
       gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
@@ -854,8 +1018,13 @@ namespace {
 template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, int WT,
           int EPI>
 hipError_t launch_one(const GemmArgs& a, int64_t total, int num_cu, hipStream_t s) {
-  constexpr size_t lds1 = (size_t)TileCfg<BM, BN, BK1, WGM, WGN, NST1, WT>::LDS;
-  constexpr size_t lds2 = BMS > 0 ? (size_t)TileCfg<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, WT>::LDS : 0;
+  using C1 = TileCfg<BM, BN, BK1, WGM, WGN, NST1, WT>;
+  using C2 = TileCfg<(BMS > 0 ? BMS : BM), BN, BK2, WGM, WGN, NST2, WT>;
+  constexpr bool AB = WT != WT_NVFP4 && WGM * WGN == 8 && BK1 == 64 && BK2 == 64 && BMS > 0;
+  constexpr size_t ab1 = AB ? (size_t)(2 * C1::A_BYTES + 3 * C1::B_BYTES) : 0;
+  constexpr size_t ab2 = AB && BMS > 0 ? (size_t)(2 * C2::A_BYTES + 3 * C2::B_BYTES) : 0;
+  constexpr size_t lds1 = (size_t)C1::LDS > ab1 ? (size_t)C1::LDS : ab1;
+  constexpr size_t lds2 = BMS > 0 ? ((size_t)C2::LDS > ab2 ? (size_t)C2::LDS : ab2) : 0;
   constexpr size_t lds = lds1 > lds2 ? lds1 : lds2;
   static_assert(lds <= 160 * 1024, "LDS");
   auto* kern = gemm_bf16_kernel<BM, BN, BMS, WGM, WGN, BK1, NST1, BK2, NST2, WT, EPI>;
