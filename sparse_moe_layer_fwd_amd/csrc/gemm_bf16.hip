@@ -767,12 +767,13 @@ __device__ __forceinline__ void gemm_stream_ab(const GemmArgs& p, char* smem, co
   const int ntn = (p.N + BN - 1) / BN;
   const int total = nrt * ntn;
   if (first >= total) return;
-  const int nk = p.K / BK;                           // >= NB (checked by the launcher)
+  const int nk = p.K / BK;                           // >= NB: the kernel takes this path only then
   char* const abase = smem;
   char* const bbase = smem + NA * C::A_BYTES;
   auto astage = [&](int t) { return abase + (t % NA) * C::A_BYTES; };
   auto bstage = [&](int t) { return bbase + (t % NB) * C::B_BYTES; };   // the B data itself
   constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
+  static_assert(C::B_PW + ST < 64, "vmcnt range");
 
   wait_vm<0>();
   TileSrc<C> cur, nxt;
