@@ -189,8 +189,56 @@ __device__ int block_excl_scan_1024(int v, int* total_out) {
   return base + x - v;
 }
 
+// Per-expert exclusive prefix over many chunks, spread over ceil(N / 64)
+// blocks: block b takes experts 64b .. 64b + 63 (one per lane) and its 16
+// wavefronts split the chunks into 16 consecutive ranges.  Each wavefront sums
+// its range, the ranges' sums are combined in LDS, then each wavefront re-reads
+// its range (now L2-resident) and writes chunk_base.  counts[e] receives the
+// expert's total.
+__global__ __launch_bounds__(1024) void chunk_prefix_kernel(const int* __restrict__ chunk_counts,
+                                                            int nchunks, int N,
+                                                            int* __restrict__ chunk_base,
+                                                            int* __restrict__ counts) {
+  __shared__ int part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int ec = min(e, N - 1);                   // lanes past N read a valid column, write nothing
+  const int per = (nchunks + 15) / 16;
+  const int c0 = min(nchunks, w * per), c1 = min(nchunks, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; c += 16) {             // 16 independent loads in flight
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {              // rows past c1 re-read row c1 - 1, value unused
+      const int x = chunk_counts[(int64_t)min(c + i, c1 - 1) * N + ec];
+      v[i] = c + i < c1 ? x : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += v[i];
+  }
+  part[w][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int u = 0; u < w; ++u) run += part[u][lane];
+  for (int c = c0; c < c1; c += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {              // rows past c1 re-read row c1 - 1, value unused
+      const int x = chunk_counts[(int64_t)min(c + i, c1 - 1) * N + ec];
+      v[i] = c + i < c1 ? x : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (c + i < c1 && e < N) chunk_base[(int64_t)(c + i) * N + e] = run;
+      run += v[i];
+    }
+  }
+  if (w == 15 && e < N) counts[e] = run;          // the sum of all 16 ranges
+}
+
 // Single block: per-expert totals over chunks (chunk_base = exclusive prefix
-// over chunks), expert offsets, and the grouped-GEMM row-tile lists.  Experts
+// over chunks; or, with nchunks == 0, the totals already in counts), expert
+// offsets, and the grouped-GEMM row-tile lists.  Experts
 // with fewer than min_rows rows get no tiles (the skinny kernel takes them).
 // With bms == 0 every other expert's rows are cut into tiles of height bm
 // (list 0).  With bms > 0 list 0 holds only full tiles of height bm and list 1
@@ -206,7 +254,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
                                                     int* __restrict__ n_tiles) {
   const int e = threadIdx.x;
   int total = 0;
-  if (e < N) {
+  if (e < N && nchunks == 0) {
+    total = counts[e];
+  } else if (e < N) {
     int c = 0;
     for (; c + 32 <= nchunks; c += 32) {          // 32 independent loads in flight
       int v[32];
@@ -254,6 +304,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
 hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
                        int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
                        int* n_tiles, hipStream_t s) {
+  if (N > 1024) return hipErrorInvalidValue;
+  if (nchunks > 32) {             // many chunks: the per-expert prefix in parallel first
+    hipLaunchKernelGGL(chunk_prefix_kernel, dim3((N + 63) / 64), dim3(1024), 0, s, chunk_counts,
+                       nchunks, N, chunk_base, counts);
+    nchunks = 0;
+  }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm, bms,
                      min_rows, chunk_base, counts, offs, tiles, tiles2, n_tiles);
   return hipGetLastError();

@@ -126,6 +126,13 @@ SMALL = {
                                 ffn=1024),
     "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
                                   top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
+    # more than 32 routing chunks of 32 tokens: the per-expert chunk prefix runs
+    # on ceil(N / 64) blocks of 16 wavefronts; 36 chunks (the last one 3 tokens)
+    # leave wavefronts 12-15 without chunks, and N = 100 / 1000 leave a partial block
+    "many_chunks_ragged": MoEConfig("many_chunks_ragged", T=1123, d=256, latent=128,
+                                    n_experts=100, top_k=5, ffn=128, zipf_s=1.1),
+    "many_chunks_max_experts": MoEConfig("many_chunks_max_experts", T=1100, d=256, latent=128,
+                                         n_experts=1000, top_k=8, ffn=128),
     # the largest N and K the ABI accepts (top-K over 1024 logits, 64 per token)
     "max_experts_max_k": MoEConfig("max_experts_max_k", T=130, d=256, latent=128, n_experts=1024,
                                    top_k=64, ffn=128),
