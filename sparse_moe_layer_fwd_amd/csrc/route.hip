@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
                                                       const float* __restrict__ add,
                                                       void* __restrict__ out) {
   const int t = blockIdx.x;
-  const int c0 = (blockIdx.y * 256 + threadIdx.x) * 8;
+  const int c0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (c0 >= W) return;
   float acc[8];
   if (add) {
@@ -405,16 +405,51 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
   }
   const int* sl = tk_slot + (int64_t)t * K;
   const float* gl = gate + (int64_t)t * K;
-  for (int k = 0; k < K; ++k) {
-    const int64_t s = sl[k];
+  // groups of G gathered rows: their loads go out together, the sums still
+  // run in k order; then the K % G rows left one at a time
+  constexpr int G = 4;
+  int k = 0;
+  for (; k + G <= K; k += G) {
+    float g[G];
+    int64_t sr[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) { sr[i] = sl[k + i]; g[i] = gl[k + i]; }
+    if (OF32) {
+      float4 a[G], b[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float4* p = reinterpret_cast<const float4*>((const float*)O + sr[i] * ldo + c0);
+        a[i] = p[0];
+        b[i] = p[1];
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        acc[0] += g[i] * a[i].x; acc[1] += g[i] * a[i].y; acc[2] += g[i] * a[i].z; acc[3] += g[i] * a[i].w;
+        acc[4] += g[i] * b[i].x; acc[5] += g[i] * b[i].y; acc[6] += g[i] * b[i].z; acc[7] += g[i] * b[i].w;
+      }
+    } else {
+      uint4 v[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[i] = *reinterpret_cast<const uint4*>((const uint16_t*)O + sr[i] * ldo + c0);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        acc[0] += g[i] * bf2f(v[i].x & 0xFFFFu); acc[1] += g[i] * bf2f(v[i].x >> 16);
+        acc[2] += g[i] * bf2f(v[i].y & 0xFFFFu); acc[3] += g[i] * bf2f(v[i].y >> 16);
+        acc[4] += g[i] * bf2f(v[i].z & 0xFFFFu); acc[5] += g[i] * bf2f(v[i].z >> 16);
+        acc[6] += g[i] * bf2f(v[i].w & 0xFFFFu); acc[7] += g[i] * bf2f(v[i].w >> 16);
+      }
+    }
+  }
+  for (; k < K; ++k) {
+    const int64_t sr = sl[k];
     const float g = gl[k];
     if (OF32) {
-      const float4* p = reinterpret_cast<const float4*>((const float*)O + s * ldo + c0);
+      const float4* p = reinterpret_cast<const float4*>((const float*)O + sr * ldo + c0);
       float4 a = p[0], b = p[1];
       acc[0] += g * a.x; acc[1] += g * a.y; acc[2] += g * a.z; acc[3] += g * a.w;
       acc[4] += g * b.x; acc[5] += g * b.y; acc[6] += g * b.z; acc[7] += g * b.w;
     } else {
-      const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)O + s * ldo + c0);
+      const uint4 v = *reinterpret_cast<const uint4*>((const uint16_t*)O + sr * ldo + c0);
       acc[0] += g * bf2f(v.x & 0xFFFFu); acc[1] += g * bf2f(v.x >> 16);
       acc[2] += g * bf2f(v.y & 0xFFFFu); acc[3] += g * bf2f(v.y >> 16);
       acc[4] += g * bf2f(v.z & 0xFFFFu); acc[5] += g * bf2f(v.z >> 16);
@@ -436,7 +471,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
 hipError_t launch_combine(const void* O, bool o_f32, int64_t ldo, const int* tk_slot,
                           const float* gate, int T, int K, int W, const float* add, void* out,
                           bool out_f32, hipStream_t s) {
-  dim3 g(T, (W + 2047) / 2048), b(256);
+  // 8 columns per thread; blocks of up to 256 threads, none idle when W <= 2048
+  const int nt = W / 8 > 192 ? 256 : ((W / 8 + 63) / 64) * 64;
+  dim3 g(T, (W + nt * 8 - 1) / (nt * 8)), b(nt);
   if (o_f32 && out_f32) hipLaunchKernelGGL((combine_kernel<true, true>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
   else if (o_f32) hipLaunchKernelGGL((combine_kernel<true, false>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
   else if (out_f32) hipLaunchKernelGGL((combine_kernel<false, true>), g, b, 0, s, O, ldo, tk_slot, gate, K, W, add, out);
