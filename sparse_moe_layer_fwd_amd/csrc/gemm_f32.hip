@@ -117,8 +117,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // BM x 128 x 32 with BM = 64 or 128, 4 wavefronts in a 2x2 grid, each
 // (BM/2) x 64 as v_mfma_f32_32x32x2_f32 blocks (4 times the MFMA work per
 // fragment read of the 64x64 tile above).  Operands are double-buffered in
-// LDS with one barrier per k-step; the next k-step's global loads sit in
-// registers while the current one is multiplied.  The sums run over k in
+// LDS with one barrier per k-step; the next k-step's global loads (for
+// 64-row tiles the next two) sit in registers while the current one is
+// multiplied.  The sums run over k in
 // ascending order within each MFMA chain, as in every other fp32 GEMM here.
 template <bool ABF16, int BM>
 __global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
@@ -134,8 +135,13 @@ __global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int rt = item / ntn, nt = item - rt * ntn;
     const int r0 = rt * BM, n0 = nt * BN;
-    f32x4 ra[BM / 32], rb[4];
-    auto load = [&](int k0) {
+    // BM = 64: two register sets, k-step ks + 2 is loaded while ks is
+    // multiplied and ks + 1 (already in registers) waits to be stored, so each
+    // load has two k-steps of MFMA work to land.  BM = 128 keeps one set (two
+    // would take it past 256 registers, to one wavefront per SIMD).
+    constexpr bool DEEP = BM == 64;
+    f32x4 ra0[BM / 32], rb0[4], ra1[BM / 32], rb1[4];
+    auto load = [&](f32x4 (&ra)[BM / 32], f32x4 (&rb)[4], int k0) {
 #pragma unroll
       for (int q = 0; q < BM / 32; ++q) {
         const int64_t row = min(r0 + lr + 32 * q, p.M - 1);
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
       for (int q = 0; q < 4; ++q)
         rb[q] = *reinterpret_cast<const f32x4*>((const float*)p.B + (int64_t)(n0 + lr + 32 * q) * p.ldb + k0 + kc);
     };
-    auto store = [&](int buf) {
+    auto store = [&](const f32x4 (&ra)[BM / 32], const f32x4 (&rb)[4], int buf) {
 #pragma unroll
       for (int q = 0; q < BM / 32; ++q)
 #pragma unroll
@@ -167,13 +173,7 @@ __global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    __syncthreads();                                     // the previous item's reads are done
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < nk) load((ks + 1) * BK);
+    auto compute = [&](int buf) {
       const float* Ab = As[buf] + (wm * (BM / 2) + (lane & 31)) * LD + (lane >> 5);
       const float* Bb = Bs[buf] + (wn * 64 + (lane & 31)) * LD + (lane >> 5);
 #pragma unroll
@@ -189,8 +189,50 @@ __global__ __launch_bounds__(256) void gemm_f32_wide_kernel(GemmArgs p) {
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
       }
-      if (ks + 1 < nk) store(buf ^ 1);
+    };
+    __syncthreads();                                     // the previous item's reads are done
+    load(ra0, rb0, 0);
+    store(ra0, rb0, 0);
+    if (!DEEP) {
       __syncthreads();
+      for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nk) load(ra0, rb0, (ks + 1) * BK);
+        compute(buf);
+        if (ks + 1 < nk) store(ra0, rb0, buf ^ 1);
+        __syncthreads();
+      }
+    } else {
+      if (nk > 1) load(ra0, rb0, BK);
+      __syncthreads();
+      // even k-steps use buffer 0 and find the next k-step in set 0; odd ones
+      // use buffer 1 and set 1.  The steady state has no branches (so the
+      // compiler's load waits stay per register set); the last 2-3 k-steps
+      // take the guarded loop.
+      int ks = 0;
+      for (; ks + 3 < nk; ks += 2) {
+        load(ra1, rb1, (ks + 2) * BK);
+        __builtin_amdgcn_sched_barrier(0);             // the loads go out before the MFMAs
+        compute(0);
+        store(ra0, rb0, 1);
+        __syncthreads();
+        load(ra0, rb0, (ks + 3) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        store(ra1, rb1, 0);
+        __syncthreads();
+      }
+      for (; ks < nk; ks += 2) {
+        if (ks + 2 < nk) load(ra1, rb1, (ks + 2) * BK);
+        compute(0);
+        if (ks + 1 < nk) store(ra0, rb0, 1);
+        __syncthreads();
+        if (ks + 1 >= nk) break;
+        if (ks + 3 < nk) load(ra0, rb0, (ks + 3) * BK);
+        compute(1);
+        if (ks + 2 < nk) store(ra1, rb1, 0);
+        __syncthreads();
+      }
     }
     // D[m][n] of each 32x32 block: n = lane % 32, m = 8 (r / 4) + 4 (lane / 32) + r % 4
 #pragma unroll
