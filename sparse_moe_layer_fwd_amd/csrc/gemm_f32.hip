@@ -294,8 +294,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)M * N) return;
   const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
+  // slices summed in order 0 .. ks-1, eight (then four) loads in flight at a time
+  const int64_t MN = (int64_t)M * N;
   float v = 0.0f;
-  for (int k = 0; k < ks; ++k) v += P[(int64_t)k * M * N + i];
+  int k = 0;
+  for (; k + 8 <= ks; k += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = P[(int64_t)(k + j) * MN + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  for (; k + 4 <= ks; k += 4) {
+    float t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = P[(int64_t)(k + j) * MN + i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v += t[j];
+  }
+  for (; k < ks; ++k) v += P[(int64_t)k * MN + i];
   v *= (p.b_gscale ? p.b_gscale[0] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f);
   const float rq = (EPI == EPI_Z8 || EPI == EPI_Q8 || EPI == EPI_SQRELU_Q8) ? 1.0f / *p.q_scale : 1.0f;
   if (EPI == EPI_F32) {
