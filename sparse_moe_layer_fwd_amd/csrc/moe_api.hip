@@ -135,21 +135,23 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
     p.bms = 0;
     p.max_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
     p.max_tiles2 = 0;
-  } else if (Tz * K >= 256 * N) {
-    // large prefill: full 256-row tiles, each expert's remaining rows in
-    // 128-row tiles.  (Sending the cold experts to the skinny kernel instead,
-    // with a 64- or 256-row cutoff, measured no faster on MI355X.)
+  } else if (Tz * K >= 128 * N) {
+    // prefill with at least 128 rows per expert on average: full 256-row
+    // tiles, each expert's remaining rows in one 128-row tile or, past 128
+    // rows, in one partial 256-row tile.  (Sending the cold experts to the
+    // skinny kernel instead, with a 64- or 256-row cutoff, measured no faster
+    // on MI355X.)  Every expert adds at most one partial tile to list 0.
     p.bm = 256;
     p.bms = kSmallBM256;
     p.cold = 0;
-    p.max_tiles = (int)((Tz * K) / p.bm);
+    p.max_tiles = (int)((Tz * K) / p.bm + N);
     p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
   } else {
-    // smaller batches: full 128-row tiles plus 64-row tiles for each
-    // expert's remainder
+    // smaller batches: full 128-row tiles plus one 64-row tile or one
+    // partial 128-row tile for each expert's remainder
     p.bm = 128;
     p.bms = kSmallBM;
-    p.max_tiles = (int)((Tz * K) / p.bm);
+    p.max_tiles = (int)((Tz * K) / p.bm + N);
     p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
   }
   size_t o = 0;

@@ -241,8 +241,9 @@ __global__ __launch_bounds__(1024) void chunk_prefix_kernel(const int* __restric
 // offsets, and the grouped-GEMM row-tile lists.  Experts
 // with fewer than min_rows rows get no tiles (the skinny kernel takes them).
 // With bms == 0 every other expert's rows are cut into tiles of height bm
-// (list 0).  With bms > 0 list 0 holds only full tiles of height bm and list 1
-// covers each expert's remaining rows with tiles of height bms.
+// (list 0).  With bms > 0 list 0 holds the full tiles of height bm and list 1
+// one tile of height bms for each expert's remaining rows; a remainder of more
+// than bms rows becomes one partial tile of list 0 instead.
 // n_tiles[0..1] = list sizes.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_counts,
                                                     int nchunks, int N, int bm, int bms, int min_rows,
@@ -279,8 +280,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   int all = 0;
   const int off = block_excl_scan_1024(total, &all);
   const bool tiled = total >= min_rows;
-  const int nbig = !tiled ? 0 : bms > 0 ? total / bm : (total + bm - 1) / bm;
-  const int rem = bms > 0 && tiled ? total - nbig * bm : 0;
+  int nbig = !tiled ? 0 : bms > 0 ? total / bm : (total + bm - 1) / bm;
+  int rem = bms > 0 && tiled ? total - nbig * bm : 0;
+  if (bms > 0 && rem > bms) {                     // one partial tile of height bm: the expert's
+    nbig += 1;                                    // weights are streamed once, not twice
+    rem = 0;
+  }
   const int nsmall = bms > 0 ? (rem + bms - 1) / bms : 0;
   int all_big = 0, all_small = 0;
   const int toff = block_excl_scan_1024(nbig, &all_big);
