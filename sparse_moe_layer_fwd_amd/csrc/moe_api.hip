@@ -135,8 +135,8 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
     p.bms = 0;
     p.max_tiles = (int)(N + (Tz * K + p.bm - 1) / p.bm);
     p.max_tiles2 = 0;
-  } else if (Tz * K >= 128 * N) {
-    // prefill with at least 128 rows per expert on average: full 256-row
+  } else if (Tz * K >= 64 * N) {
+    // prefill with at least 64 rows per expert on average: full 256-row
     // tiles, each expert's remaining rows in one 128-row tile or, past 128
     // rows, in one partial 256-row tile.  (Sending the cold experts to the
     // skinny kernel instead, with a 64- or 256-row cutoff, measured no faster
