@@ -35,7 +35,7 @@ constexpr int kTokensPerChunk = 32;   // routing chunk: one histogram row / one 
 constexpr int kF32BM = 64;            // fp32 GEMM row-tile height
 constexpr int kSmallBM = 64;          // grouped bf16 GEMM: height of each expert's remainder tiles
 constexpr int kSmallBM256 = 128;      // ... when the full tiles are 256 rows high
-constexpr int kSkinnyMaxT = 64;       // at most this many rows per expert -> skinny path
+constexpr int kSkinnyMaxT = 128;      // batches up to this many tokens -> skinny path
 // split-K partial buffer: floats per CU (two blocks of 64 x 64 outputs)
 constexpr size_t kPartialPerCu = 2 * 64 * 64;
 

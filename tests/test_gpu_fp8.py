@@ -80,6 +80,9 @@ FP8_SMALL = {
     "fp8_decode_max_experts_max_k": MoEConfig("fp8_decode_max_experts_max_k", T=20, d=256,
                                               latent=256, n_experts=1024, top_k=64, ffn=256,
                                               expert="fp8"),
+    # skinny expert kernel above 64 tokens: several 64-row chunks per hot expert
+    "fp8_skinny_multi_chunk": MoEConfig("fp8_skinny_multi_chunk", T=120, d=512, latent=512,
+                                        n_experts=8, top_k=4, ffn=512, expert="fp8", zipf_s=1.1),
     "fp8_multi_item": MoEConfig("fp8_multi_item", T=8192, d=256, latent=256, n_experts=8,
                                 top_k=4, ffn=1024, expert="fp8", zipf_s=1.1),
 }

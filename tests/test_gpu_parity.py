@@ -126,6 +126,13 @@ SMALL = {
                                 ffn=1024),
     "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
                                   top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
+    # small batches above 64 tokens on the skinny expert kernel: experts with
+    # more than 64 rows run it in several 64-row chunks
+    "skinny_multi_chunk_bf16": MoEConfig("skinny_multi_chunk_bf16", T=128, d=512, latent=256,
+                                         n_experts=8, top_k=4, ffn=512, zipf_s=1.1),
+    "skinny_multi_chunk_nvfp4": MoEConfig("skinny_multi_chunk_nvfp4", T=100, d=512, latent=256,
+                                          n_experts=8, top_k=4, ffn=512, expert="nvfp4",
+                                          zipf_s=1.1),
     # more than 32 routing chunks of 32 tokens: the per-expert chunk prefix runs
     # on ceil(N / 64) blocks of 16 wavefronts; 36 chunks (the last one 3 tokens)
     # leave wavefronts 12-15 without chunks, and N = 100 / 1000 leave a partial block
