@@ -210,14 +210,17 @@ int split_factor(int64_t tiles, int K, int kstep, int min_slice, int num_cu) {
   return ks;
 }
 
-// Dense bf16 GEMM.  Small batches (M <= 64) run on the skinny kernel with K
+// Dense bf16 GEMM.  Small batches (M <= 64, or M <= 128 when the output has
+// fewer than num_cu / 8 tiles of 128 x 128) run on the skinny kernel with K
 // split across blocks (weights streamed by every CU); larger ones on the
 // largest tile that still gives every CU work.
 // fp8: A and B are E4M3 codes (the shared experts of an FP8 layer).
 hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, float* P, hipStream_t s,
                       bool fp8 = false) {
-  if (a.M <= 64 && a.N % 64 == 0 && a.K % 256 == 0 && a.kseg >= a.K) {
-    const int ks = split_factor(a.N / 64, a.K, 256, 256, num_cu);
+  const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if ((a.M <= 64 || (a.M <= 128 && t128 * 8 < num_cu)) && a.N % 64 == 0 && a.K % 256 == 0 &&
+      a.kseg >= a.K) {
+    const int ks = split_factor((int64_t)(a.N / 64) * ((a.M + 63) / 64), a.K, 256, 256, num_cu);
     if ((size_t)ks * a.M * a.N <= kPartialPerCu * (size_t)num_cu)   // always, unless N is huge
       return launch_skinny_splitk(a, fp8, epi, ks, P, s);
   }

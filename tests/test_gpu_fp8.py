@@ -80,6 +80,11 @@ FP8_SMALL = {
     "fp8_decode_max_experts_max_k": MoEConfig("fp8_decode_max_experts_max_k", T=20, d=256,
                                               latent=256, n_experts=1024, top_k=64, ffn=256,
                                               expert="fp8"),
+    # 100 tokens: projections and FP8 shared experts on the split-K skinny
+    # kernel over two 64-row chunks
+    "fp8_shared_split_k_two_chunks": MoEConfig("fp8_shared_split_k_two_chunks", T=100, d=512,
+                                               latent=256, n_experts=16, top_k=4, ffn=256,
+                                               n_shared=1, shared_ffn=512, shared_fp8=True),
     # skinny expert kernel above 64 tokens: several 64-row chunks per hot expert
     "fp8_skinny_multi_chunk": MoEConfig("fp8_skinny_multi_chunk", T=120, d=512, latent=512,
                                         n_experts=8, top_k=4, ffn=512, expert="fp8", zipf_s=1.1),
