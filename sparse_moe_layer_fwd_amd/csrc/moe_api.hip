@@ -210,7 +210,7 @@ int split_factor(int64_t tiles, int K, int kstep, int min_slice, int num_cu) {
   return ks;
 }
 
-// Dense bf16 GEMM.  Small batches (M <= 64, or M <= 128 when the output has
+// Dense bf16 GEMM.  Small batches (M <= 64, or M <= 256 when the output has
 // fewer than num_cu / 8 tiles of 128 x 128) run on the skinny kernel with K
 // split across blocks (weights streamed by every CU); larger ones on the
 // largest tile that still gives every CU work.
@@ -218,7 +218,7 @@ int split_factor(int64_t tiles, int K, int kstep, int min_slice, int num_cu) {
 hipError_t dense_bf16(const GemmArgs& a, int epi, int num_cu, float* P, hipStream_t s,
                       bool fp8 = false) {
   const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if ((a.M <= 64 || (a.M <= 128 && t128 * 8 < num_cu)) && a.N % 64 == 0 && a.K % 256 == 0 &&
+  if ((a.M <= 64 || (a.M <= 256 && t128 * 8 < num_cu)) && a.N % 64 == 0 && a.K % 256 == 0 &&
       a.kseg >= a.K) {
     const int ks = split_factor((int64_t)(a.N / 64) * ((a.M + 63) / 64), a.K, 256, 256, num_cu);
     if ((size_t)ks * a.M * a.N <= kPartialPerCu * (size_t)num_cu)   // always, unless N is huge
