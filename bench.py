@@ -5,7 +5,7 @@ One step = one moe_forward over a batch of T tokens: down-projection, fp32
 router, top-K/softmax, expert histogram/scan/scatter, the two grouped expert
 GEMMs, combine and up-projection, all in libmoe.so on HBM-resident inputs.
 
-    python bench.py [--config 3] [--steps 20] [--warmup 5] [--gpus 1]
+    python bench.py [--config 5] [--steps 20] [--warmup 5] [--gpus 1]
     python bench.py --paired      # standard vs latent at the ablation shapes
     python bench.py --paired router_at_d   # router on the latent vs on x at d
 
@@ -46,6 +46,17 @@ def expert_weight_bytes_per_matrix(cfg):
     if cfg.expert == "fp8":
         return el + 4
     return el * (4 if cfg.expert == "f32" else 2)
+
+
+def expert_kernel(cfg):
+    """The kernel the library runs the grouped expert GEMMs on: the skinny
+    kernel for batches of up to 128 tokens when l and m are multiples of 256,
+    the tiled MFMA kernel otherwise (fp32 kernel for an all-fp32 layer)."""
+    if cfg.act == "f32":
+        return "gemm_f32_kernel"
+    if cfg.T <= 128 and cfg.latent % 256 == 0 and cfg.ffn % 256 == 0:
+        return "skinny_kernel"
+    return "gemm_bf16_kernel"
 
 
 def layer_bytes(cfg, touched):
@@ -286,7 +297,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="layer configuration 1-13 (default 3)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="layer configuration 1-13 (default 5: the Ultra-like NVFP4 prefill layer, "
+                         "the largest configuration on one GPU)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,9 +371,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
                 "frac": round(ach / peak_f, 4), "traffic": None}
     roof["traffic"] = measured_traffic(cfg.name)
-    roof.update({"kernel": "grouped expert GEMM (%s)" % ("skinny_kernel" if cfg.T <= 64 and cfg.act != "f32"
-                                                         else "gemm_bf16_kernel" if cfg.act != "f32"
-                                                         else "gemm_f32_kernel"),
+    roof.update({"kernel": "grouped expert GEMM (%s)" % expert_kernel(cfg),
                  "launches": launches, "avg_launch_ms": round(avg_ms, 5),
                  "algorithmic_flops_per_launch": flops_launch,
                  "algorithmic_bytes_per_launch": bytes_launch})

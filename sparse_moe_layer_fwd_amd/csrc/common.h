@@ -111,7 +111,6 @@ struct SkinnyArgs {
   const float* a_scale; const float* q_scale;
   int32_t N, K;
   const int* counts; const int* offs;
-  int32_t max_rows;                                   // experts with >= max_rows rows are skipped
   void* C; int64_t ldc;
   float* P; int64_t p_slice;                          // split-K partials: slice s at P + s * p_slice
 };
@@ -124,9 +123,11 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool a_is_bf16, int epi, int grid_
 // Every dimension of the fp32 kernel: K % (32 * ks) == 0.
 hipError_t launch_gemm_f32_splitk(const GemmArgs& a, bool a_is_bf16, int epi, int ks, float* P,
                                   hipStream_t s);
-// bf16 or FP8 (fp8: A and B E4M3 codes) dense GEMM with M <= 64 on the
-// skinny kernel, K split into ks slices (K % (256 * ks) == 0, N % 64 == 0),
-// then the same sum and epilogue.
+// bf16 or FP8 (fp8: A and B E4M3 codes) dense GEMM of a small batch on the
+// skinny kernel over ceil(M / 64) chunks of 64 rows, K split into ks slices
+// (K % (256 * ks) == 0, N % 64 == 0), then the same sum and epilogue.  The
+// dispatcher sends M <= 64 here, and M <= 256 when the output has fewer than
+// num_cu / 8 tiles of 128 x 128.
 hipError_t launch_skinny_splitk(const GemmArgs& a, bool fp8, int epi, int ks, float* P, hipStream_t s);
 // out = epi( sum over the ks slices of P ), one thread per output element
 hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float* P, hipStream_t s);
@@ -141,7 +142,7 @@ hipError_t launch_quant_fp8(const uint16_t* in, int64_t n, const float* scale, u
                             hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms,
                        int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
                        int* n_tiles, hipStream_t s);
 hipError_t launch_scatter(const int* idx, int T, int K, int N, int tc, const int* chunk_base,

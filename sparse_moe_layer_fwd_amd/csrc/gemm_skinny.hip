@@ -1,5 +1,5 @@
-// Skinny grouped expert GEMM: experts with few rows.  That is every expert in
-// batch decode (T <= 64) and the cold experts of a skewed prefill batch.  Here
+// Skinny grouped expert GEMM: experts with few rows, every expert of a batch
+// of up to 128 tokens (batch decode).  Here
 // the work is bound by streaming the expert's weights from HBM (the pages:
 // latency-bound serving of tens to hundreds of tokens is dominated by expert
 // weight traffic; Korean Nemotron 3 summary, section 2.2 LatentMoE), so the
@@ -83,7 +83,7 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
+#pragma nounroll
   for (int kb = kw0; kb < kw0 + kq; kb += KS) {
     const int k = kb + grp * 8 * NCH;
     uint4 b[4][NCH];
@@ -199,15 +199,14 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
   }
 }
 
-// Grid (column tiles of 64, experts).  An expert with 0 < count < max_rows is
-// processed in chunks of up to 64 rows; larger experts are left to the tiled
-// GEMM.
+// Grid (column tiles of 64, experts).  Each expert's rows are processed in
+// chunks of up to 64 rows.
 template <int WT, int EPI, bool WIDE = false>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   __shared__ float red[3][16][4][64];                    // partial sums of waves 1..3
   const int e = blockIdx.y;
   const int cnt = p.counts[e];
-  if (cnt == 0 || cnt >= p.max_rows) return;
+  if (cnt == 0) return;
   const int row0 = p.offs[e];
   for (int c0 = 0; c0 < cnt; c0 += 64) {
     skinny_chunk<WT, EPI, WIDE>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);

@@ -100,7 +100,6 @@ struct Plan {
   size_t z32, z16, z8, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
   size_t slot_token, tk_slot, H, O, u, x8, Hs, ys, partial, total;
   int nchunks, bm, bms, max_tiles, max_tiles2;
-  int cold;        // prefill: experts with fewer rows go to the skinny kernel (0: none)
   bool f32, skinny;
   bool fp8;        // FP8 routed experts: E4M3 latent rows z8 and hidden rows H
   bool sfp8;       // FP8 shared experts: E4M3 x8 and hidden rows Hs
@@ -143,7 +142,6 @@ Plan make_plan(const moe_config_t& c, int T, int num_cu) {
     // on MI355X.)  Every expert adds at most one partial tile to list 0.
     p.bm = 256;
     p.bms = kSmallBM256;
-    p.cold = 0;
     p.max_tiles = (int)((Tz * K) / p.bm + N);
     p.max_tiles2 = (int)std::min<size_t>(N * (size_t)(p.bm / p.bms), N + (Tz * K + p.bms - 1) / p.bms);
   } else {
@@ -318,7 +316,7 @@ int enqueue_routing(moe_handle_t h, const void* x, int T, void* ws, const Plan& 
                         at<int>(ws, p.idx), at<float>(ws, p.gate), at<int>(ws, p.ccount), s));
   }
   StageScope sc(MOE_STAGE_SCAN, s);
-  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, p.bms, p.cold,
+  MOE_TRY(launch_scan(at<int>(ws, p.ccount), p.nchunks, c.n_experts, p.bm, p.bms,
                       at<int>(ws, p.cbase), at<int>(ws, p.counts), at<int>(ws, p.offs),
                       at<int4>(ws, p.tiles), at<int4>(ws, p.tiles2), at<int>(ws, p.ntiles), s));
   return MOE_OK;
@@ -363,7 +361,6 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   sk.b_gscale = G; sk.a_scale = as; sk.q_scale = qs;
   sk.N = (int)rows; sk.K = (int)kdim;
   sk.counts = at<int>(ws, p.counts); sk.offs = at<int>(ws, p.offs);
-  sk.max_rows = p.skinny ? INT32_MAX : p.cold;
   sk.C = C; sk.ldc = rows;
   const int epi = up ? (fp8 ? EPI_SQRELU_Q8 : EPI_SQRELU_BF16) : EPI_BF16;
   if (p.skinny) {
@@ -390,7 +387,6 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   const int64_t ntn = (rows + bn - 1) / bn;
   const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
   MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
-  if (p.cold > 0) MOE_TRY(launch_skinny(sk, wt, epi, c.n_experts, s));
   return MOE_OK;
 }
 

@@ -238,15 +238,14 @@ __global__ __launch_bounds__(1024) void chunk_prefix_kernel(const int* __restric
 
 // Single block: per-expert totals over chunks (chunk_base = exclusive prefix
 // over chunks; or, with nchunks == 0, the totals already in counts), expert
-// offsets, and the grouped-GEMM row-tile lists.  Experts
-// with fewer than min_rows rows get no tiles (the skinny kernel takes them).
-// With bms == 0 every other expert's rows are cut into tiles of height bm
+// offsets, and the grouped-GEMM row-tile lists.
+// With bms == 0 every expert's rows are cut into tiles of height bm
 // (list 0).  With bms > 0 list 0 holds the full tiles of height bm and list 1
 // one tile of height bms for each expert's remaining rows; a remainder of more
 // than bms rows becomes one partial tile of list 0 instead.
 // n_tiles[0..1] = list sizes.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_counts,
-                                                    int nchunks, int N, int bm, int bms, int min_rows,
+                                                    int nchunks, int N, int bm, int bms,
                                                     int* __restrict__ chunk_base,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offs,
@@ -279,9 +278,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   }
   int all = 0;
   const int off = block_excl_scan_1024(total, &all);
-  const bool tiled = total >= min_rows;
-  int nbig = !tiled ? 0 : bms > 0 ? total / bm : (total + bm - 1) / bm;
-  int rem = bms > 0 && tiled ? total - nbig * bm : 0;
+  int nbig = bms > 0 ? total / bm : (total + bm - 1) / bm;
+  int rem = bms > 0 ? total - nbig * bm : 0;
   if (bms > 0 && rem > bms) {                     // one partial tile of height bm: the expert's
     nbig += 1;                                    // weights are streamed once, not twice
     rem = 0;
@@ -306,7 +304,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
   }
 }
 
-hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms, int min_rows,
+hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms,
                        int* chunk_base, int* counts, int* offs, int4* tiles, int4* tiles2,
                        int* n_tiles, hipStream_t s) {
   if (N > 1024) return hipErrorInvalidValue;
@@ -316,7 +314,7 @@ hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int 
     nchunks = 0;
   }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, N, bm, bms,
-                     min_rows, chunk_base, counts, offs, tiles, tiles2, n_tiles);
+                     chunk_base, counts, offs, tiles, tiles2, n_tiles);
   return hipGetLastError();
 }
 
