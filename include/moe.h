@@ -149,6 +149,23 @@ int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gat
 int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
                 int32_t* counts, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the whole
+ * layer exactly as moe_forward (same kernels, bitwise the same outputs), with
+ * the workspace taken from the library's own device array of
+ * MOE_SCRATCH_BYTES bytes instead of a caller buffer.  Each GPU the library
+ * runs on holds one such array from the first moe_init on that device until the
+ * process ends; the call allocates and frees nothing and records no stage
+ * timer events.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (each call initialises what it reads), so calls that overlap
+ * on one GPU (several streams, host threads or handles) race: serialise them.
+ * Returns MOE_ERR_WORKSPACE when moe_workspace_size(h, T) exceeds
+ * MOE_SCRATCH_BYTES (decode batches fit: e.g. T = 128 at d = 8192, l = m =
+ * 2048, 512 experts, top-22 needs about 33 MB), else as moe_forward. */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
+                        int32_t* counts, void* stream);
+
 /* Quantise n bf16 values (device, 16-byte aligned) to OCP FP8 E4M3 codes
  * (device, 16-byte aligned) with the per-tensor scale *scale (device fp32):
  * the FP8 input rule above.  For callers preparing FP8 weights or activations.

@@ -16,7 +16,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_NO_
 MOE_F32, MOE_BF16, MOE_NVFP4, MOE_FP8 = 0, 1, 2, 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "fp8": MOE_FP8}
 
-EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_quantize_fp8",
+EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_forward_noalloc",
+            "moe_quantize_fp8",
             "moe_destroy", "moe_status_string", "moe_profile_enable", "moe_profile_read",
             "moe_stage_name")
 MOE_NUM_STAGES = 11
@@ -62,6 +63,8 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.moe_route.restype = ctypes.c_int
     L.moe_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp]
+    L.moe_forward_noalloc.restype = ctypes.c_int
     L.moe_quantize_fp8.argtypes = [vp, ctypes.c_int64, vp, vp, vp]
     L.moe_quantize_fp8.restype = ctypes.c_int
     L.moe_destroy.argtypes = [vp]
@@ -116,6 +119,16 @@ def moe_forward(h, x, T, y, idx, gate, counts, ws, ws_bytes, stream, check: bool
     if check:
         _check(st, "moe_forward")
     return st
+
+
+def moe_forward_noalloc(h, x, T, y, idx, gate, counts, stream, check: bool = True) -> int:
+    st = lib().moe_forward_noalloc(h, x, int(T), y, idx, gate, counts, stream)
+    if check:
+        _check(st, "moe_forward_noalloc")
+    return st
+
+
+MOE_SCRATCH_BYTES = 64 << 20     # include/moe.h
 
 
 def moe_quantize_fp8(x, n, scale, out, stream, check: bool = True) -> int:

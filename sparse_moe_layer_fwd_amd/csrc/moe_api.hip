@@ -27,7 +27,15 @@ struct moe_handle {
   moe_weights_t w;
   int device;
   int num_cu;
+  void* scratch;     // this device's copy of `scratch` (device address)
 };
+
+// Workspace of moe_forward_noalloc: a file-scope device array, one copy per GPU
+// (allocated when the library's code object is loaded on that device and held
+// until the process ends).  Host code never uses its name as an address: the
+// name is a host-side stand-in; each device's address comes from
+// hipGetSymbolAddress, taken once per device at moe_init.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
 
 namespace {
 
@@ -43,6 +51,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // ---- optional stage timing: a HIP event pair around each stage ----
+// moe_forward_noalloc records no stage events (event creation is a host-side
+// allocation the no-allocation entry point avoids)
+thread_local bool tls_no_stage_events = false;
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -69,6 +80,7 @@ hipEvent_t prof_event() {
 }
 // Records the start of a stage; returns the index of its record or -1.
 int prof_begin(int stage, hipStream_t s) {
+  if (tls_no_stage_events) return -1;
   Prof& P = prof();
   std::lock_guard<std::mutex> g(P.mu);
   if (!P.on) return -1;
@@ -95,6 +107,32 @@ struct StageScope {
   ~StageScope() { prof_end(rec, s); }
 };
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// once per device.
+constexpr int kMaxDevices = 64;
+struct ScratchTable {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+ScratchTable& scratch_table() {
+  static ScratchTable* t = new ScratchTable;   // never destroyed: safe at process exit
+  return *t;
+}
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchTable& T = scratch_table();
+  std::lock_guard<std::mutex> g(T.mu);
+  if (!T.ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+    T.ptr[dev] = p;
+  }
+  *out = T.ptr[dev];
+  return hipSuccess;
+}
 
 struct Plan {
   size_t z32, z16, z8, logits, idx, gate, ccount, cbase, counts, offs, tiles, tiles2, ntiles;
@@ -390,6 +428,9 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   return MOE_OK;
 }
 
+int forward_impl(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
+                 int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -482,12 +523,15 @@ int moe_init(const moe_config_t* cfg, const moe_weights_t* w, moe_handle_t* out)
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MOE_ERR_HIP;
+  void* sp = nullptr;
+  if (scratch_address(dev, &sp) != hipSuccess) return MOE_ERR_HIP;
   moe_handle* h = new (std::nothrow) moe_handle;
   if (!h) return MOE_ERR_INVALID_ARG;
   h->c = c;
   h->w = *w;
   h->device = dev;
   h->num_cu = ncu > 0 ? ncu : 256;
+  h->scratch = sp;
   *out = h;
   return MOE_OK;
 }
@@ -566,6 +610,26 @@ int moe_route(moe_handle_t h, const void* x, int32_t T, int32_t* idx, float* gat
 
 int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
                 int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(h, x, T, y, idx, gate, counts, ws, ws_bytes, stream);
+}
+
+int moe_forward_noalloc(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
+                        float* gate, int32_t* counts, void* stream) {
+  if (!h) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > h->c.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && make_plan(h->c, T, h->num_cu).total > MOE_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  tls_no_stage_events = true;
+  const int st = forward_impl(h, x, T, y, idx, gate, counts, h->scratch, MOE_SCRATCH_BYTES, stream);
+  tls_no_stage_events = false;
+  return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+int forward_impl(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx, float* gate,
+                 int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
   int st = check_call(h, x, T, ws, ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
@@ -649,4 +713,4 @@ int moe_forward(moe_handle_t h, const void* x, int32_t T, void* y, int32_t* idx,
   return copy_out(h, T, ws, p, idx, gate, counts, s);
 }
 
-}  // extern "C"
+}  // namespace

@@ -167,6 +167,25 @@ class DeviceLayer:
             return y, idx, gate, counts
         return y
 
+    def forward_noalloc(self, x: torch.Tensor, y=None, routing: bool = False, stream=None):
+        """moe_forward_noalloc: the library's own scratch array as the workspace."""
+        T = x.shape[0]
+        dev = x.device
+        if y is None:
+            y = torch.empty((T, self.cfg.d), dtype=self.act_torch_dtype(), device=dev)
+        idx = gate = counts = None
+        if routing:
+            K, N = self.cfg.top_k, self.cfg.n_experts
+            idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+            gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+            counts = torch.empty((N,), dtype=torch.int32, device=dev)
+        s = (stream or torch.cuda.current_stream(dev)).cuda_stream
+        B.moe_forward_noalloc(self.handle, x.data_ptr(), T, y.data_ptr(), _ptr(idx), _ptr(gate),
+                              _ptr(counts), s)
+        if routing:
+            return y, idx, gate, counts
+        return y
+
 
 def x_to_device(wl: Workload, device="cuda") -> torch.Tensor:
     return host_tensor(wl.x(), wl.cfg.act).to(device)
