@@ -9,9 +9,9 @@
 // straight from z by token id).  B is bf16 or NVFP4: NVFP4 codes (E2M1 values,
 // 16-element E4M3 block scales, FP32 global scale; Korean Nemotron 3 summary,
 // section 2.4 NVFP4 Training) are staged raw in LDS and decoded exactly to bf16
-// in registers by each wavefront right before its MFMAs (every e2m1*e4m3
-// product is a bf16 value); the global scale multiplies the fp32 accumulator in
-// the epilogue.  Or both operands are FP8 E4M3 codes (FP8 post-training
+// (as half their value) in registers by each wavefront right before its MFMAs
+// (every e2m1*e4m3 product is a bf16 value); twice the global scale multiplies
+// the fp32 accumulator in the epilogue.  Or both operands are FP8 E4M3 codes (FP8 post-training
 // quantisation of weights and activations, Nemotron 3 Nano blog, FP8
 // quantisation section; FP8 shared experts, Ultra release news): the loads and
 // LDS layout are those of a bf16 GEMM over K/2 (two codes per 16-bit slot),
@@ -100,34 +100,42 @@ __device__ __forceinline__ int swz_chunk(int row, int c) {
   return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
 }
 
-// NVFP4 decode with the gfx950 conversion v_cvt_scalef32_pk_bf16_fp4, which
-// turns one byte (two E2M1 codes, low nibble first) into two bf16 multiplied by
-// the power of two in its scale operand (only the scale's exponent is used).
-// The E4M3 block scale s = 2^E * f is applied as 2^E in the conversion and f
-// (a 4-bit significand with s's sign) as one fp32 multiply; both steps are
-// exact because every e2m1 * e4m3 product fits in bf16.
+// NVFP4 decode.  A block scale s (E4M3) is converted exactly to fp32 by the
+// hardware (v_cvt_scalef32_f32_fp8, unit scale).  The gfx950 conversion
+// v_cvt_scalef32_pk_f32_fp4 turns one byte (two E2M1 codes, low nibble first)
+// into two fp32 values multiplied by the power of two of its scale operand
+// (only the operand's exponent is used); given |s| it applies
+// 2^floor(log2|s|), and one fp32 multiply by frexp_mant(s) = s / 2^(floor+1)
+// (in [0.5, 1) with s's sign, 0 when s = 0) completes the product.  The result
+// is w / 2 for the element's true value w = e2m1 * s: exact, since every
+// e2m1 * e4m3 product has at most 6 significant bits; the factor 2 is folded
+// into the epilogue's fp32 scale.  The pair is packed to bf16 by taking the
+// high halves (exact values, so truncation is exact).
 struct Fp4Scale {
   float pow2, frac;
 };
-__device__ __forceinline__ Fp4Scale split_scale(uint32_t e4m3) {
-  const float s = e4m3_to_f32(e4m3);
-  const uint32_t b = __float_as_uint(s);
+// byte 0 of `sbyte` is the E4M3 scale
+__device__ __forceinline__ Fp4Scale split_scale(uint32_t sbyte) {
+  const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sbyte, 1.0f, 0);
   Fp4Scale r;
-  r.pow2 = __uint_as_float(b & 0x7F800000u);
-  r.frac = s == 0.0f ? 0.0f : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+  r.pow2 = __builtin_fabsf(s);
+  r.frac = __builtin_amdgcn_frexp_mantf(s);
   return r;
 }
 template <int BYTE>
 __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, const Fp4Scale& sc) {
-  const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc.pow2, BYTE));
-  const float lo = __uint_as_float(pr << 16) * sc.frac;
-  const float hi = __uint_as_float(pr & 0xFFFF0000u) * sc.frac;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc.pow2, BYTE);
+  const float lo = v.x * sc.frac, hi = v.y * sc.frac;
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
-// 8 codes (one dword) -> 8 bf16 (one uint4)
+// 8 codes (one dword) -> 8 bf16 (one uint4), each half its true value
 __device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
   return make_uint4(fp4_pair<0>(w, sc), fp4_pair<1>(w, sc), fp4_pair<2>(w, sc), fp4_pair<3>(w, sc));
 }
+// the epilogue factor that undoes the halving of decoded NVFP4 weights
+template <int WT>
+constexpr float decode_factor() { return WT == WT_NVFP4 ? 2.0f : 1.0f; }
 
 }  // namespace
 
@@ -376,7 +384,8 @@ __device__ __forceinline__ void epilogue_tile(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   // weight scale times activation scale (1 for bf16 operands)
-  const float sc = (p.b_gscale ? sload(p.b_gscale + g) : 1.0f) * (p.a_scale ? sload(p.a_scale) : 1.0f);
+  const float sc = (p.b_gscale ? sload(p.b_gscale + g) : 1.0f) * (p.a_scale ? sload(p.a_scale) : 1.0f) *
+                   decode_factor<WT>();
   const float rq = K::Q8 ? 1.0f / sload(p.q_scale) : 1.0f;
   if constexpr (K::STAGED) {
     constexpr int EL = K::ELEM;
@@ -518,7 +527,7 @@ template <class C>
 __device__ __forceinline__ void mma_fp4_frags(const Fp4Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j] & 0xFFu)));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j])));
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
       acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
