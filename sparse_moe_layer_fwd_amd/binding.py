@@ -45,11 +45,16 @@ class MoEError(RuntimeError):
 _LIB = None
 
 
-def lib(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmoe.so (once).  Raises FileNotFoundError if it was not built."""
+def lib(path: str = None) -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises FileNotFoundError if it was not built.
+
+    The path defaults to the in-tree build; the environment variable
+    MOE_LIBRARY may name another build of the same library (the CPU-side
+    sanitizer build used by the ABI tests)."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    path = path or os.environ.get("MOE_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise FileNotFoundError("libmoe.so not built at %s (run python -m sparse_moe_layer_fwd_amd.build)"
                                 % path)
