@@ -565,7 +565,9 @@ __device__ __forceinline__ void interleave_reads_mfma() {
 // waits leave the previous epilogue's stores in flight until a k-tile issued
 // after them is needed.  NVFP4 stages hold the raw codes and scales; each
 // wavefront decodes the B fragments it multiplies (those of its wavefront
-// column), so the decode runs on the VALU beside the other wavefront's MFMAs.
+// column; with a 1 x 8 wavefront grid each element is decoded by one
+// wavefront), so the decode runs on the VALU beside the other wavefront's
+// MFMAs.
 template <int BM, int BN, int BK, int WGM, int WGN, int NST, int EPI>
 __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, const int4* list,
                                                 int nrt, int first, int step) {
@@ -1130,8 +1132,8 @@ hipError_t launch_shape(const GemmArgs& a, int wt, int epi, int64_t grid, int nu
 
 }  // namespace
 
-// Tile shapes: 256x256 (8 wavefronts, 2x4), 256x128 and 128x128 (4 wavefronts,
-// 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height
+// Tile shapes: 256x256 (8 wavefronts, 2x4; 1x8 for grouped NVFP4 weights),
+// 256x128 and 128x128 (4 wavefronts, 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height
 // bm, list 1 of height bms; max_items bounds the items for the grid size.
 hipError_t launch_gemm_bf16(const GemmArgs& a0, int wt, int epi, int bm, int bn, int bms,
                             int64_t max_items, int num_cu, hipStream_t s) {
@@ -1153,6 +1155,13 @@ hipError_t launch_gemm_bf16(const GemmArgs& a0, int wt, int epi, int bm, int bn,
     if (bm == 128 && bn == 128) return launch_shape<128, 128, 0, 2, 2>(a, wt, epi, total, num_cu, s);
     return hipErrorInvalidValue;
   }
+  // NVFP4 weights: the 8 wavefronts side by side along the weight columns
+  // (wavefront tile 256 x 32), so each decoded B fragment feeds 8 MFMAs
+  // instead of 4 and every weight element is decoded once per tile, at twice
+  // the A-fragment LDS reads (measured 3.5% faster than 2 x 4 on the Ultra-like
+  // NVFP4 prefill's grouped GEMMs)
+  if (bm == 256 && bn == 256 && bms == 128 && wt == WT_NVFP4)
+    return launch_shape<256, 256, 128, 1, 8>(a, wt, epi, total, num_cu, s);
   if (bm == 256 && bn == 256 && bms == 128) return launch_shape<256, 256, 128, 2, 4>(a, wt, epi, total, num_cu, s);
   if (bm == 128 && bn == 128 && bms == 64) return launch_shape<128, 128, 64, 2, 2>(a, wt, epi, total, num_cu, s);
   return hipErrorInvalidValue;
