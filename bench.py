@@ -175,7 +175,23 @@ class GpuTelemetry:
         return r
 
 
-def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0):
+def forced_workload(cfg, seed):
+    """The layer's workload with every token routed to the same K experts
+    (experts 0, N/K, 2N/K, ...: a large router bias on them): every expert GEMM
+    then runs full-height row tiles only, a dense-like ablation of the same
+    layer and FLOPs."""
+    import numpy as np
+    from sparse_moe_layer_fwd_amd.workloads import Workload
+
+    class Forced(Workload):
+        def b_router(self):
+            b = np.zeros(cfg.n_experts, np.float32)
+            b[np.arange(cfg.top_k) * (cfg.n_experts // cfg.top_k)] = 50.0
+            return b
+    return Forced(cfg, seed)
+
+
+def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=False):
     """Build the layer with seeded weights, warm up, then time `steps`
     back-to-back moe_forward calls on the current stream (inputs resident in
     HBM) with the library's per-stage timer on."""
@@ -187,7 +203,7 @@ def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0):
     dev = torch.device("cuda:0")
     log("bench: config %d %s, generating weights" % (cfg_id, cfg.name))
     t0 = time.perf_counter()
-    wl = Workload(cfg, seed)
+    wl = forced_workload(cfg, seed) if forced else Workload(cfg, seed)
     layer = DeviceLayer.from_workload(wl, device=dev, threads=16)
     x = x_to_device(wl, dev)
     y = torch.empty((cfg.T, cfg.d), dtype=layer.act_torch_dtype(), device=dev)
@@ -310,6 +326,10 @@ def main():
                     help="time a pair of layers instead: 'ablation' (standard vs latent, "
                          "configurations 6/3 and 7/8), 'router_at_d' (3/9 and 8/10) or 'fp8' "
                          "(bf16 vs FP8 experts, 3/11 and 4/12)")
+    ap.add_argument("--expert-dtype", choices=["bf16", "nvfp4", "fp8"], default=None,
+                    help="ablation: the chosen layer with its routed experts in another storage type")
+    ap.add_argument("--forced-routing", action="store_true",
+                    help="ablation: every token routed to the same K experts (full row tiles only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
@@ -344,7 +364,12 @@ def main():
         return
 
     cfg = CONFIGS[args.config]
-    r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup, args.telemetry_ms)
+    if args.expert_dtype and args.expert_dtype != cfg.expert:
+        cfg = cfg.replace(name=cfg.name + "+%s_experts" % args.expert_dtype, expert=args.expert_dtype)
+    if args.forced_routing:
+        cfg = cfg.replace(name=cfg.name + "+forced_routing")
+    r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup, args.telemetry_ms,
+                   forced=args.forced_routing)
     ms_step, stages, counts_np, touched = r["ms_step"], r["stages"], r["counts"], r["touched"]
 
     # dominant kernel: the grouped expert GEMMs (two launches per step)
