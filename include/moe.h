@@ -87,12 +87,12 @@ typedef struct {
   const void* w_down;      /* [l][d] act dtype; NULL unless has_latent_proj          */
   const float* w_router;   /* [N][l] fp32 ([N][d] when router_on_x)                  */
   const float* b_router;   /* [N] fp32 added to the logits before top-K, or NULL     */
-  const void* w1;          /* [N][m][l]; NVFP4: packed codes uint8 [N][m][l/2];
+  const void* w1;          /* [N][m][l]; NVFP4: codes uint8, k-tiled [N][l/64][m][32];
                               FP8: E4M3 codes uint8 [N][m][l]                  */
-  const void* w2;          /* [N][l][m]; NVFP4: packed codes uint8 [N][l][m/2];
+  const void* w2;          /* [N][l][m]; NVFP4: codes uint8, k-tiled [N][m/64][l][32];
                               FP8: E4M3 codes uint8 [N][l][m]                  */
-  const uint8_t* w1_scale; /* NVFP4 only: E4M3 bytes [N][m][l/16], else NULL          */
-  const uint8_t* w2_scale; /* NVFP4 only: E4M3 bytes [N][l][m/16], else NULL          */
+  const uint8_t* w1_scale; /* NVFP4 only: E4M3 bytes, k-tiled [N][l/64][m][4], else NULL */
+  const uint8_t* w2_scale; /* NVFP4 only: E4M3 bytes, k-tiled [N][m/64][l][4], else NULL */
   const float* w1_gscale;  /* NVFP4: [N] fp32 global scales; FP8: [N] fp32 per-matrix
                               weight scales; else NULL                          */
   const float* w2_gscale;  /* as w1_gscale, for W2                                  */
@@ -108,9 +108,15 @@ typedef struct {
   const float* shared_act_scale; /* shared_fp8: [2] fp32 per-tensor scales of x and
                               of the shared hidden activations; else NULL     */
 } moe_weights_t;
-/* NVFP4 packing: element 2j of a row in the low nibble of byte j, element 2j+1
- * in the high nibble; block b of a row covers elements 16b..16b+15 along the
- * reduction dimension; w = e2m1(code) * e4m3(scale) * gscale[expert].
+/* NVFP4 packing: w = e2m1(code) * e4m3(scale) * gscale[expert], one E4M3
+ * scale per block of 16 elements along the reduction dimension.  The weights
+ * are k-tiled: a matrix of R rows (output features) and reduction length Kr
+ * is stored as Kr/64 slabs; slab t holds, for each row r in order, 32 code
+ * bytes and, in the scale array, 4 scale bytes (byte b: block 4t+b, elements
+ * 64t+16b .. 64t+16b+15).  Code bytes 16h+4i .. 16h+4i+3 (h = 0, 1; i =
+ * 0..3) hold elements 64t+16i+8h .. 64t+16i+8h+7, two per byte, the lower
+ * element in the low nibble.  moe_nvfp4_tile converts row-major codes (byte j
+ * of a row: elements 2j, low nibble, and 2j+1) and scales to this layout.
  * FP8 (OCP E4M3: bias 7, no infinities, 448 the largest finite value, S.1111.111
  * NaN): a weight is e4m3(code) * its matrix scale.  An FP8 GEMM input v with
  * per-tensor scale a is quantised as code = RNE_e4m3(clamp(fp32(v) * r, -448,
@@ -171,6 +177,18 @@ int moe_forward_noalloc(moe_handle_t h, const void* x, int32_t T, void* y, int32
  * the FP8 input rule above.  For callers preparing FP8 weights or activations.
  * n must be a multiple of 16; n == 0 enqueues nothing.  Enqueued on `stream`. */
 int moe_quantize_fp8(const void* in, int64_t n, const float* scale, uint8_t* out, void* stream);
+
+/* Convert NVFP4 weights of n_mats matrices of `rows` rows and reduction length
+ * k from row-major codes [n_mats][rows][k/2] and scales [n_mats][rows][k/16]
+ * (device) to the k-tiled layout above (device, caller-allocated, same sizes).
+ * A byte permutation run once when weights are loaded (NVFP4 format: E2M1
+ * elements, E4M3 block scales of 16; Korean Nemotron 3 summary, section 2.4
+ * NVFP4 Training).  k must be a multiple of 64 and rows >= 1; all four
+ * pointers 16-byte aligned, the outputs overlapping neither input nor each
+ * other (MOE_ERR_INVALID_ARG otherwise).  n_mats == 0 enqueues nothing.
+ * Enqueued on `stream`. */
+int moe_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_tiled,
+                   uint8_t* scales_tiled, int64_t n_mats, int32_t rows, int32_t k, void* stream);
 
 /* Release a handle (host memory only).  NULL is accepted. */
 int moe_destroy(moe_handle_t h);

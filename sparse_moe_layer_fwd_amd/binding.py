@@ -17,7 +17,7 @@ MOE_F32, MOE_BF16, MOE_NVFP4, MOE_FP8 = 0, 1, 2, 3
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "nvfp4": MOE_NVFP4, "fp8": MOE_FP8}
 
 EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_forward_noalloc",
-            "moe_quantize_fp8",
+            "moe_quantize_fp8", "moe_nvfp4_tile",
             "moe_destroy", "moe_status_string", "moe_profile_enable", "moe_profile_read",
             "moe_stage_name")
 MOE_NUM_STAGES = 11
@@ -72,6 +72,8 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.moe_forward_noalloc.restype = ctypes.c_int
     L.moe_quantize_fp8.argtypes = [vp, ctypes.c_int64, vp, vp, vp]
     L.moe_quantize_fp8.restype = ctypes.c_int
+    L.moe_nvfp4_tile.argtypes = [vp, vp, vp, vp, ctypes.c_int64, i32, i32, vp]
+    L.moe_nvfp4_tile.restype = ctypes.c_int
     L.moe_destroy.argtypes = [vp]
     L.moe_destroy.restype = ctypes.c_int
     L.moe_status_string.argtypes = [ctypes.c_int]
@@ -140,6 +142,15 @@ def moe_quantize_fp8(x, n, scale, out, stream, check: bool = True) -> int:
     st = lib().moe_quantize_fp8(x, int(n), scale, out, stream)
     if check:
         _check(st, "moe_quantize_fp8")
+    return st
+
+
+def moe_nvfp4_tile(codes, scales, codes_tiled, scales_tiled, n_mats, rows, k, stream,
+                   check: bool = True) -> int:
+    st = lib().moe_nvfp4_tile(codes, scales, codes_tiled, scales_tiled, int(n_mats), int(rows), int(k),
+                              stream)
+    if check:
+        _check(st, "moe_nvfp4_tile")
     return st
 
 

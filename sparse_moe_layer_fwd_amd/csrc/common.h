@@ -92,6 +92,8 @@ struct GemmArgs {
   const void* B; int64_t ldb; int64_t b_gstride;     // element units (bf16/f32) or bytes (fp4 codes)
   int32_t kseg; int64_t b_segstride;                  // k split into segments of kseg (shared W2)
   const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;  // NVFP4 scales
+  // NVFP4 weights are k-tiled (codes [K/64][N][32 B], scales [K/64][N][4 B]
+  // per group): ldb and lds_scale are the byte strides of one 64-deep k-slab
   const float* b_gscale;                              // NVFP4 / FP8 per-group weight scale
   const float* a_scale;                               // FP8 A: per-tensor scale (device scalar)
   const float* q_scale;                               // FP8 outputs: per-tensor scale
@@ -105,7 +107,7 @@ struct GemmArgs {
 
 struct SkinnyArgs {
   const void* A; int64_t lda; const int* a_rows;      // bf16, or E4M3 codes with FP8 weights
-  const void* B; int64_t ldb; int64_t b_gstride;
+  const void* B; int64_t ldb; int64_t b_gstride;      // NVFP4: k-tiled as in GemmArgs
   const uint8_t* b_scale; int64_t lds_scale; int64_t s_gstride;
   const float* b_gscale;
   const float* a_scale; const float* q_scale;
@@ -140,6 +142,9 @@ hipError_t launch_skinny(const SkinnyArgs& a, int wt, int epi, int n_experts, hi
 // out[i] = E4M3 code of in[i] / *scale (in bf16), n % 16 == 0
 hipError_t launch_quant_fp8(const uint16_t* in, int64_t n, const float* scale, uint8_t* out,
                             hipStream_t s);
+// NVFP4 row-major codes/scales -> the k-tiled layout (quant.hip)
+hipError_t launch_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_t,
+                             uint8_t* scales_t, int64_t n_mats, int rows, int k, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int N, int K, int tc, int* idx, float* gate,
                        int* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int* chunk_counts, int nchunks, int N, int bm, int bms,

@@ -137,6 +137,12 @@ __device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
 template <int WT>
 constexpr float decode_factor() { return WT == WT_NVFP4 ? 2.0f : 1.0f; }
 
+// NVFP4 codes of a 64-deep k-slab in a stage: row r's 32 bytes as two
+// 16-byte halves (the k-tiled layout puts the codes of k 16i + 8h .. + 7, i =
+// 0..3, in half h); half h sits in slot h ^ fp4_slot_swz(r), so that the
+// 16-byte fragment reads of 8 (or 16) consecutive rows fall in distinct banks.
+__device__ __forceinline__ int fp4_slot_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+
 }  // namespace
 
 template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT>
@@ -144,8 +150,9 @@ struct TileCfg {
   static constexpr bool FP4 = WT == WT_NVFP4, IS_FP4 = FP4, IS_FP8 = WT == WT_FP8;
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per bf16 row
+  static constexpr int KSUB = BK / 16;                         // 16-deep MFMA substeps per k-tile
   static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int BQ_BYTES = BN * BK / 2;                 // NVFP4 codes
+  static constexpr int BQ_BYTES = BN * 32;                     // NVFP4 codes: the whole 64-deep slab
   static constexpr int BS_BYTES = BN * 4;                      // NVFP4 scales: one aligned dword per row
   static constexpr int B_BYTES = FP4 ? BQ_BYTES + BS_BYTES : BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -167,6 +174,7 @@ struct TileCfg {
   static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(TM >= 1 && TN >= 1, "wave tile");
   static_assert(!IS_FP8 || BK % 32 == 0, "FP8: whole 64-code steps per k-tile");
+  static_assert(!FP4 || BK == 64 || BK == 32, "NVFP4: k-tiles of 32 or 64 in 64-deep weight slabs");
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -292,12 +300,13 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
   for (int j = 0; j < C::B_PW; ++j) {
     const int blk = (wave + j * NW) % C::B_TOT;
     if (FP4) {
-      // codes: 16 bytes (32 k) per DMA chunk, stored chunk-major in LDS
-      // ([32-k chunk][row][16 B]) so that the 32 rows of a fragment read hit
-      // 16 banks at most twice
-      const int q = blk * 64 + lane, row = q % BN, pos = q / BN;
+      // k-tiled codes: a 64-deep k-slab holds every row's 32 bytes in row
+      // order; a DMA block is 32 rows x 32 bytes (two lanes per row, halves
+      // swizzled).  A 32-deep k-tile loads its whole slab too.  Offsets are
+      // relative to the slab.
+      const int q = blk * 64 + lane, row = q >> 1;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
-      s.boff[j] = n * (uint32_t)p.ldb + pos * 16;  // bytes
+      s.boff[j] = n * 32u + (uint32_t)(((q & 1) ^ fp4_slot_swz(row)) * 16);
     } else {
       const int q = blk * 64 + lane, row = q / CPR, pos = q % CPR;
       const uint32_t n = (uint32_t)min(n0 + row, p.N - 1);
@@ -308,8 +317,8 @@ __device__ __forceinline__ void make_src(const GemmArgs& p, int g, int r0, int r
   for (int j = 0; j < C::S_PW1; ++j) {
     const int blk = (wave + j * NW) % C::S_TOT1;
     const uint32_t n = (uint32_t)min(n0 + blk * 64 + lane, p.N - 1);
-    s.soff[j] = n * (uint32_t)p.lds_scale;         // bytes; the k-tile's BK/16 scale bytes sit
-                                                   // in the aligned dword loaded per row
+    s.soff[j] = n * 4u;                            // bytes in the k-slab: the row's dword holds
+                                                   // the slab's four block scales
   }
 }
 
@@ -334,15 +343,17 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
   if constexpr (!(PARTS & 2)) {
     return;
   } else if (FP4) {
+    const uint32_t slab = k0 / 64;
+    const char* Bk = s.B + slab * (uint32_t)p.ldb;
 #pragma unroll
     for (int j = 0; j < C::B_PW; ++j) {
       const int blk = (wave + j * NW) % C::B_TOT;
-      dma16(s.B + k0 / 2, s.boff[j], stage + C::A_BYTES + blk * 1024);
+      dma16(Bk, s.boff[j], stage + C::A_BYTES + blk * 1024);
     }
 #pragma unroll
     for (int j = 0; j < C::S_PW; ++j) {
       const int blk = (wave + j * NW) % C::S_TOT1;
-      dma_small<4>(s.S + ((k0 / 16) & ~3u), s.soff[j], stage + C::A_BYTES + C::BQ_BYTES + blk * 256);
+      dma_small<4>(s.S + slab * (uint32_t)p.lds_scale, s.soff[j], stage + C::A_BYTES + C::BQ_BYTES + blk * 256);
     }
   } else {
     const char* Bk = s.B + k0 * 2;
@@ -499,63 +510,90 @@ __device__ __forceinline__ i32x8 lds_pair(const uint4* base, int c0, int c1) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// NVFP4 pipeline: operand fragments of one 16-wide k substep for one
-// wavefront.  The B fragments stay raw (8 codes and their block scale) until
-// the MFMAs use them.
+// NVFP4 pipeline.  Substep s of a k-tile covers k 16s .. 16s + 15, lane half
+// h its 8 k from 16s + 8h (A chunk 2s + h), as in the bf16 kernels.  In the
+// k-tiled layout those codes of every substep are one 16-byte half of the
+// row's slab, so a lane reads its codes once per k-tile (BK/4 bytes), and its
+// block scales as one dword.
 template <class C>
-struct Fp4Frags {
+struct Fp4A {
   bf16x8 a[C::TM];
-  uint32_t bq[C::TN], bs[C::TN];
+};
+template <class C>
+struct Fp4B {
+  uint32_t q[C::TN][C::KSUB];   // raw codes: dword s feeds substep s
+  uint32_t sc[C::TN];           // the row's block scales (E4M3) of the slab
 };
 
-// Fragments of substep s of the k-tile in `stage`.  kbyte: position of the
-// k-tile's first scale byte in the aligned scale dword of each row.
+// A fragments of substep s of the k-tile in `stage`.
 template <int BM, int BN, int BK, int WGM, int WGN, int NST>
-__device__ __forceinline__ void read_fp4_frags(const char* stage, int s, int kbyte,
-                                               Fp4Frags<TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>>& f) {
+__device__ __forceinline__ void read_fp4_a(const char* stage, int s,
+                                           Fp4A<TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>>& f) {
   using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>;
-  constexpr int CPR = C::CPR, WM = C::WM, WN = C::WN;
+  constexpr int CPR = C::CPR, WM = C::WM;
   const uint4* As = reinterpret_cast<const uint4*>(stage);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+  const int wm = wave / WGN;
   const int ch = s * 2 + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int row = wm * WM + i * 32 + (lane & 31);
     f.a[i] = __builtin_bit_cast(bf16x8, As[row * CPR + swz_chunk<CPR>(row, ch)]);
   }
-  // lane half h takes k 8h..8h+7 of the substep: 4 code bytes at byte
-  // 8(s & 1) + 4h of 32-k chunk s / 2
+}
+
+// Raw B fragments (codes and scales) of the k-tile in `stage`; odd: a 32-deep
+// k-tile in the slab's second half.
+template <int BM, int BN, int BK, int WGM, int WGN, int NST>
+__device__ __forceinline__ void read_fp4_b(const char* stage, int odd,
+                                           Fp4B<TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>>& f) {
+  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT_NVFP4>;
+  constexpr int WN = C::WN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % WGN, h = lane >> 5;
   const uint8_t* Q = reinterpret_cast<const uint8_t*>(stage + C::A_BYTES);
   const uint8_t* Sc = Q + C::BQ_BYTES;
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
     const int n = wn * WN + j * 32 + (lane & 31);
-    f.bq[j] = *reinterpret_cast<const uint32_t*>(Q + (((s >> 1) * BN + n) << 4) + ((s & 1) << 3) +
-                                                 ((lane >> 5) << 2));
-    f.bs[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4) >> (8 * (kbyte + s));
+    const uint8_t* half = Q + n * 32 + ((h ^ fp4_slot_swz(n)) << 4);
+    if constexpr (BK == 64) {
+      const uint4 v = *reinterpret_cast<const uint4*>(half);
+      f.q[j][0] = v.x; f.q[j][1] = v.y; f.q[j][2] = v.z; f.q[j][3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(half + 8 * odd);
+      f.q[j][0] = v.x; f.q[j][1] = v.y;
+    }
+    f.sc[j] = *reinterpret_cast<const uint32_t*>(Sc + n * 4);
   }
 }
 
-// acc += fragments (the MFMA computes C^T: weights as its A operand); the B
-// fragments are decoded here, exactly, to bf16.
+// The decoded (exact) bf16 B fragments of substep s; kbyte: position of the
+// k-tile's first block scale in the scale dword.
 template <class C>
-__device__ __forceinline__ void mma_fp4_frags(const Fp4Frags<C>& f, f32x16 (&acc)[C::TN][C::TM]) {
+__device__ __forceinline__ void decode_fp4_b(const Fp4B<C>& f, int s, int kbyte, bf16x8 (&b)[C::TN]) {
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, fp4x8(f.bq[j], split_scale(f.bs[j])));
+  for (int j = 0; j < C::TN; ++j)
+    b[j] = __builtin_bit_cast(bf16x8, fp4x8(f.q[j][s], split_scale(f.sc[j] >> (8 * (kbyte + s)))));
+}
+
+// acc += A fragments x decoded B fragments (the MFMA computes C^T: weights as
+// its A operand).
+template <class C>
+__device__ __forceinline__ void mma_fp4(const Fp4A<C>& f, const bf16x8 (&b)[C::TN], f32x16 (&acc)[C::TN][C::TM]) {
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
-      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, f.a[i], acc[j][i], 0, 0, 0);
-  }
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], f.a[i], acc[j][i], 0, 0, 0);
 }
 
-// Scheduling constraint for one substep: alternate the next substep's LDS
-// reads with this substep's MFMAs, so each read's latency hides behind MFMAs
-// instead of stalling the wavefront before the first of them.
-template <class C>
+// Scheduling constraint for one substep: alternate NR LDS reads (the next
+// substep's fragments) with this substep's MFMAs, so each read's latency hides
+// behind MFMAs instead of stalling the wavefront before the first of them.
+template <class C, int NR>
 __device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int NR = C::TM + 2 * C::TN, NM = C::TM * C::TN;
+  constexpr int NM = C::TM * C::TN;
   constexpr int P = NR < NM ? NR : NM;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
@@ -609,10 +647,13 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
   int issued = NST;          // k-tiles of this stream issued so far
   wait_tiles<C::LOADS, NST - 1>(issued - 1);
   bar();
-  Fp4Frags<C> f0, f1;
-  // the aligned scale dword of each row holds k-tile kt's first scale at this byte
+  Fp4A<C> f0, f1;          // A fragments of alternate substeps
+  Fp4B<C> fb;              // raw B fragments of the current k-tile
+  // the scale dword of each row holds k-tile kt's first block scale at this
+  // byte (a slab's 4 blocks hold two 32-deep k-tiles)
   auto kbyte = [](int kt) { return (kt * (BK / 16)) & 3; };
-  read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(smem, 0, 0, f0);
+  read_fp4_a<BM, BN, BK, WGM, WGN, NST>(smem, 0, f0);
+  read_fp4_b<BM, BN, BK, WGM, WGN, NST>(smem, 0, fb);
   int gt = 0;                // k-tiles of this stream consumed so far
   // stores per thread of one staged epilogue (all issued, see epilogue_tile)
   constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
@@ -646,14 +687,16 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
       const char* st = smem + sg * C::STAGE;
 #pragma unroll
       for (int s = 0; s + 1 < S; ++s) {
+        bf16x8 b[TN];
+        decode_fp4_b<C>(fb, s, kbyte(kt), b);
         if (s % 2 == 0) {
-          read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, kbyte(kt), f1);
-          mma_fp4_frags<C>(f0, acc);
+          read_fp4_a<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f1);
+          mma_fp4<C>(f0, b, acc);
         } else {
-          read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(st, s + 1, kbyte(kt), f0);
-          mma_fp4_frags<C>(f1, acc);
+          read_fp4_a<BM, BN, BK, WGM, WGN, NST>(st, s + 1, f0);
+          mma_fp4<C>(f1, b, acc);
         }
-        interleave_reads_mfma<C>();
+        interleave_reads_mfma<C, TM>();
         if (pend_j >= 0) {
           if (s == 0) issue_a_range<BM, BN, BK, WGM, WGN, NST, WT, 0, (S == 2 ? C::A_PW : AH)>(cur, pend_j, pend_st);
           if (s == 1) issue_a_range<BM, BN, BK, WGM, WGN, NST, WT, AH, C::A_PW>(cur, pend_j, pend_st);
@@ -668,6 +711,7 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
       const int j = kt + NST;
       char* fs = smem + sg * C::STAGE;
       int refill = 0;                    // 1: k-tile j of this item, 2: k-tile j - nk of the next
+      const char* nst = smem + ((gt + 1) % NST) * C::STAGE;
       if (kt + 1 < nk || has_next) {
         // k-tile gt + 1 landed (own loads), own reads of stage sg complete;
         // after the barrier the same holds for every wavefront
@@ -684,13 +728,19 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
           ++issued;
         }
         if (FIRST == 3) refill = 0;
-        read_fp4_frags<BM, BN, BK, WGM, WGN, NST>(smem + ((gt + 1) % NST) * C::STAGE, 0,
-                                                   kbyte(kt + 1 < nk ? kt + 1 : 0), f0);
+        read_fp4_a<BM, BN, BK, WGM, WGN, NST>(nst, 0, f0);
       }
       // one call site for the last substep: duplicating it in both branches
-      // doubles the live accumulators and spills them
-      mma_fp4_frags<C>(f1, acc);
-      interleave_reads_mfma<C>();
+      // doubles the live accumulators and spills them.  Its B fragments are
+      // decoded first, then the next k-tile's raw ones read into the same
+      // registers (in the stream's last k-tile a harmless read of a stale stage)
+      {
+        bf16x8 b[TN];
+        decode_fp4_b<C>(fb, S - 1, kbyte(kt), b);
+        read_fp4_b<BM, BN, BK, WGM, WGN, NST>(nst, kt + 1 < nk ? (kt + 1) & 1 : 0, fb);
+        mma_fp4<C>(f1, b, acc);
+      }
+      interleave_reads_mfma<C, TM + 2 * TN>();
       // refill 1 (j < nk: the next k-tile is this item's): A part over the
       // next k-tile's substeps; refill 2: at once
       if (refill == 1) { pend_j = j; pend_st = fs; }

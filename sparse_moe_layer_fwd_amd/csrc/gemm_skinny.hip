@@ -65,9 +65,9 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int n = min(n0 + cb * 16 + (lane & 15), p.N - 1);
-    if (FP4) {
-      brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb;
-      srow[cb] = p.b_scale + (int64_t)e * p.s_gstride + (int64_t)n * p.lds_scale;
+    if (FP4) {                                           // k-tiled: row n of k-slab 0
+      brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * 32;
+      srow[cb] = p.b_scale + (int64_t)e * p.s_gstride + (int64_t)n * 4;
     } else if (FP8) {
       brow[cb] = (const uint8_t*)p.B + (int64_t)e * p.b_gstride + (int64_t)n * p.ldb;
       srow[cb] = nullptr;
@@ -91,8 +91,13 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       if (FP4) {
-        const uint2 c = *reinterpret_cast<const uint2*>(brow[cb] + k / 2);
-        const float s = e4m3_to_f32(srow[cb][k / 16]);
+        // the step's 64 k are one k-slab: the lane's 16 codes (dwords 2 grp and
+        // 2 grp + 1 of the row, stored at positions grp and 4 + grp) and their scale
+        const int64_t slab = kb / 64;
+        const uint8_t* bs = brow[cb] + slab * p.ldb + grp * 4;
+        const uint2 c = make_uint2(*reinterpret_cast<const uint32_t*>(bs),
+                                   *reinterpret_cast<const uint32_t*>(bs + 16));
+        const float s = e4m3_to_f32(srow[cb][slab * p.lds_scale + grp]);
         b[cb][0] = make_uint4(fp4x2_bf(c.x & 0xFFu, s), fp4x2_bf((c.x >> 8) & 0xFFu, s),
                               fp4x2_bf((c.x >> 16) & 0xFFu, s), fp4x2_bf(c.x >> 24, s));
         b[cb][1] = make_uint4(fp4x2_bf(c.y & 0xFFu, s), fp4x2_bf((c.y >> 8) & 0xFFu, s),

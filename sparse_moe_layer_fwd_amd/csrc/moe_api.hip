@@ -393,9 +393,10 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   memset(&sk, 0, sizeof(sk));
   sk.A = (const uint16_t*)A; sk.lda = kdim; sk.a_rows = a_rows;
   sk.B = B;
-  sk.ldb = fp4 ? kdim / 2 : kdim;
+  // NVFP4 (k-tiled): ldb and lds_scale are the byte strides of one 64-deep k-slab
+  sk.ldb = fp4 ? rows * 32 : kdim;
   sk.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
-  sk.b_scale = S; sk.lds_scale = kdim / 16; sk.s_gstride = rows * kdim / 16;
+  sk.b_scale = S; sk.lds_scale = rows * 4; sk.s_gstride = rows * kdim / 16;
   sk.b_gscale = G; sk.a_scale = as; sk.q_scale = qs;
   sk.N = (int)rows; sk.K = (int)kdim;
   sk.counts = at<int>(ws, p.counts); sk.offs = at<int>(ws, p.offs);
@@ -408,9 +409,9 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   GemmArgs a = gemm_args();
   a.A = A; a.lda = kdim; a.a_rows = a_rows;
   a.B = B;
-  a.ldb = fp4 ? kdim / 2 : kdim;
+  a.ldb = fp4 ? rows * 32 : kdim;
   a.b_gstride = fp4 ? rows * kdim / 2 : rows * kdim;
-  a.b_scale = S; a.lds_scale = kdim / 16; a.s_gstride = rows * kdim / 16;
+  a.b_scale = S; a.lds_scale = rows * 4; a.s_gstride = rows * kdim / 16;
   a.b_gscale = G; a.a_scale = as; a.q_scale = qs;
   a.N = (int)rows; a.K = (int)kdim;
   a.tiles = at<int4>(ws, p.tiles); a.n_tiles = at<int>(ws, p.ntiles);
@@ -587,6 +588,27 @@ int moe_quantize_fp8(const void* in, int64_t n, const float* scale, uint8_t* out
   if (!in || !out || !scale || !aligned16(in) || !aligned16(out) || !aligned4(scale))
     return MOE_ERR_INVALID_ARG;
   MOE_TRY(launch_quant_fp8((const uint16_t*)in, n, scale, out, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_tiled,
+                   uint8_t* scales_tiled, int64_t n_mats, int32_t rows, int32_t k, void* stream) {
+  if (n_mats < 0 || rows < 1 || k < 64 || k % 64 != 0) return MOE_ERR_INVALID_ARG;
+  if (n_mats == 0) return MOE_OK;
+  if (!codes || !scales || !codes_tiled || !scales_tiled || !aligned16(codes) || !aligned16(scales) ||
+      !aligned16(codes_tiled) || !aligned16(scales_tiled))
+    return MOE_ERR_INVALID_ARG;
+  // the outputs must not overlap the inputs
+  const uintptr_t cb = (uintptr_t)n_mats * rows * (k / 2), sb = (uintptr_t)n_mats * rows * (k / 16);
+  auto overlap = [](const void* a, uintptr_t an, const void* b, uintptr_t bn) {
+    return (uintptr_t)a < (uintptr_t)b + bn && (uintptr_t)b < (uintptr_t)a + an;
+  };
+  if (overlap(codes, cb, codes_tiled, cb) || overlap(codes, cb, scales_tiled, sb) ||
+      overlap(scales, sb, codes_tiled, cb) || overlap(scales, sb, scales_tiled, sb) ||
+      overlap(codes_tiled, cb, scales_tiled, sb))
+    return MOE_ERR_INVALID_ARG;
+  MOE_TRY(launch_nvfp4_tile(codes, scales, codes_tiled, scales_tiled, n_mats, rows, k,
+                            (hipStream_t)stream));
   return MOE_OK;
 }
 

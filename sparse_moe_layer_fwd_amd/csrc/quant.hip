@@ -36,4 +36,41 @@ hipError_t launch_quant_fp8(const uint16_t* in, int64_t n, const float* scale, u
   return hipGetLastError();
 }
 
+// NVFP4 weights from row-major codes [mats][rows][k/2] and scales
+// [mats][rows][k/16] to the k-tiled layout the expert GEMMs stream: for each
+// matrix, 64-deep k-slab t holds every row's 32 code bytes (elements 64t ..
+// 64t + 63) in row order, and every row's 4 scale bytes (blocks 4t .. 4t + 3)
+// likewise.  Within a row's 32 bytes the dwords (8 codes each) go in the
+// order 0, 2, 4, 6, 1, 3, 5, 7: half h then holds the codes of k 16i + 8h ..
+// + 7 for i = 0..3, which one lane half of a GEMM wavefront consumes.  A pure
+// permutation of bytes; thread i moves one (matrix, slab, row), consecutive
+// threads consecutive rows of one slab.
+__global__ __launch_bounds__(256) void nvfp4_tile_kernel(const uint4* __restrict__ codes,
+                                                         const uint32_t* __restrict__ scales,
+                                                         uint4* __restrict__ codes_t,
+                                                         uint32_t* __restrict__ scales_t,
+                                                         int64_t total, int rows, int slabs) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i % rows, ms = i / rows;           // ms = matrix * slabs + slab
+    const int64_t e = ms / slabs, t = ms - e * slabs;
+    const int64_t src = (e * rows + r) * slabs + t;      // 32-byte unit of the row-major codes
+    const uint4 a = codes[2 * src], b = codes[2 * src + 1];   // dwords 0-3, 4-7
+    codes_t[2 * i] = make_uint4(a.x, a.z, b.x, b.z);
+    codes_t[2 * i + 1] = make_uint4(a.y, a.w, b.y, b.w);
+    scales_t[i] = scales[src];
+  }
+}
+
+hipError_t launch_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_t,
+                             uint8_t* scales_t, int64_t n_mats, int rows, int k, hipStream_t s) {
+  if (n_mats < 0 || rows < 1 || k < 64 || k % 64 != 0) return hipErrorInvalidValue;
+  const int64_t total = n_mats * rows * (int64_t)(k / 64);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const int grid = (int)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(nvfp4_tile_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)codes,
+                     (const uint32_t*)scales, (uint4*)codes_t, (uint32_t*)scales_t, total, rows, k / 64);
+  return hipGetLastError();
+}
+
 }  // namespace moe

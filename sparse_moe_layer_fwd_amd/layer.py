@@ -111,8 +111,13 @@ class DeviceLayer:
                     else:
                         full[e].copy_(host_tensor(part, cfg.expert))
             if cfg.expert == "nvfp4":
-                t[which] = codes
-                t[which + "_scale"] = scales
+                # the library reads NVFP4 weights k-tiled: permute on the device
+                tiled = torch.empty_like(codes), torch.empty_like(scales)
+                B.moe_nvfp4_tile(_ptr(codes), _ptr(scales), _ptr(tiled[0]), _ptr(tiled[1]), N, rows,
+                                 cols, torch.cuda.current_stream(dev).cuda_stream)
+                torch.cuda.synchronize(dev)
+                del codes, scales
+                t[which], t[which + "_scale"] = tiled
                 t[which + "_gscale"] = torch.from_numpy(gs).to(dev)
             elif cfg.expert == "fp8":
                 t[which] = codes

@@ -140,6 +140,20 @@ def test_quantize_fp8_argument_checks(lib):
     assert lib.moe_quantize_fp8(FAKE, 16, FAKE + 1, FAKE, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_nvfp4_tile_argument_checks(lib):
+    A, Bp, C, D = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20)
+    assert lib.moe_nvfp4_tile(A, Bp, C, D, 0, 8, 64, None) == B.MOE_OK          # nothing to do
+    assert lib.moe_nvfp4_tile(A, Bp, C, D, 1, 8, 96, None) == B.MOE_ERR_INVALID_ARG   # k % 64
+    assert lib.moe_nvfp4_tile(A, Bp, C, D, 1, 8, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_nvfp4_tile(A, Bp, C, D, 1, 0, 64, None) == B.MOE_ERR_INVALID_ARG   # rows
+    assert lib.moe_nvfp4_tile(A, Bp, C, D, -1, 8, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_nvfp4_tile(None, Bp, C, D, 1, 8, 64, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_nvfp4_tile(A, Bp, C + 4, D, 1, 8, 64, None) == B.MOE_ERR_INVALID_ARG  # alignment
+    assert lib.moe_nvfp4_tile(A, Bp, A, D, 1, 8, 64, None) == B.MOE_ERR_INVALID_ARG       # in place
+    assert lib.moe_nvfp4_tile(A, Bp, A + 128, D, 1, 8, 64, None) == B.MOE_ERR_INVALID_ARG  # overlap
+    assert lib.moe_nvfp4_tile(A, Bp, C, C + 16, 1, 8, 64, None) == B.MOE_ERR_INVALID_ARG  # outputs overlap
+
+
 def test_calls_on_null_handle(lib):
     n = ctypes.c_size_t()
     assert lib.moe_workspace_size(None, 4, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG
