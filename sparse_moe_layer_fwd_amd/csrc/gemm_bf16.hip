@@ -369,22 +369,6 @@ __device__ __forceinline__ void issue_tile(const GemmArgs& p,
   }
 }
 
-// The A part of k-tile kt, blocks LO .. HI-1 of this wavefront's A_PW, into
-// `stage` (the NVFP4 stream issues an A refill in pieces over the substeps of
-// the k-tile after the one that freed its stage).
-template <int BM, int BN, int BK, int WGM, int WGN, int NST, int WT, int LO, int HI>
-__device__ __forceinline__ void issue_a_range(const TileSrc<TileCfg<BM, BN, BK, WGM, WGN, NST, WT>>& s,
-                                              int kt, char* stage) {
-  using C = TileCfg<BM, BN, BK, WGM, WGN, NST, WT>;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t k0 = (uint32_t)kt * BK;
-#pragma unroll
-  for (int j = LO; j < (HI < C::A_PW ? HI : C::A_PW); ++j) {
-    const int blk = (wave + j * C::NW) % C::A_TOT;
-    dma16(s.A + k0 * 2, s.aoff[j], stage + blk * 1024);
-  }
-}
-
 // Epilogue.  acc[j][i][r] = C[row][col] with row = i-block row (lane & 31),
 // col = j-block column 8*(r/4) + 4*(lane/32) + r%4: 4 consecutive columns per r/4.
 // bf16 and E4M3 outputs go through LDS (`stage`, EPB bytes): a lane's own
@@ -658,16 +642,6 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
   // stores per thread of one staged epilogue (all issued, see epilogue_tile)
   constexpr int ST = EpiKind<EPI>::STAGED ? TM * (32 * WGM * (BN * EpiKind<EPI>::ELEM / 16)) / C::NT : 0;
   int st_tile = -1;          // last k-tile issued before the latest epilogue's stores
-  // The A part of a refill whose k-tile belongs to this item is issued in two
-  // pieces after substeps 0 and 1 of the next k-tile rather than at once
-  // (measured ~1% faster): k-tile pend_j into stage pend_st.  Its loads still
-  // go out before that k-tile's wait, after its own B part and before the next
-  // refill's, so every k-tile's loads stay one contiguous group for the vmcnt
-  // waits.  A refill of the next item's k-tile (before an epilogue's stores)
-  // is issued whole, as the waits that count those stores require.
-  int pend_j = -1;
-  char* pend_st = smem;
-  constexpr int AH = (C::A_PW + 1) / 2;
 
   for (;;) {
     const int itn = it + step;
@@ -697,16 +671,12 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
           mma_fp4<C>(f1, b, acc);
         }
         interleave_reads_mfma<C, TM>();
-        if (pend_j >= 0) {
-          if (s == 0) issue_a_range<BM, BN, BK, WGM, WGN, NST, WT, 0, (S == 2 ? C::A_PW : AH)>(cur, pend_j, pend_st);
-          if (s == 1) issue_a_range<BM, BN, BK, WGM, WGN, NST, WT, AH, C::A_PW>(cur, pend_j, pend_st);
-          if (s == 1 || S == 2) pend_j = -1;
-        }
       }
       // refill stage sg with the k-tile NST ahead.  With 8 wavefronts the
       // weight codes and scales go out right after the barrier and the A rows
       // after the last substep (measured 3-4% faster than the reverse order on
-      // the Ultra-like NVFP4 prefill; everything after the barrier was slower)
+      // the Ultra-like NVFP4 prefill, everything after the barrier 2-3% slower,
+      // the A rows spread over the next k-tile's first substeps 1.5-2.5% slower)
       constexpr int FIRST = C::NW == 8 ? 2 : 3;
       const int j = kt + NST;
       char* fs = smem + sg * C::STAGE;
@@ -741,9 +711,8 @@ __device__ __forceinline__ void gemm_stream_fp4(const GemmArgs& p, char* smem, c
         mma_fp4<C>(f1, b, acc);
       }
       interleave_reads_mfma<C, TM + 2 * TN>();
-      // refill 1 (j < nk: the next k-tile is this item's): A part over the
-      // next k-tile's substeps; refill 2: at once
-      if (refill == 1) { pend_j = j; pend_st = fs; }
+      // the A part of the refill: k-tile j of this item or j - nk of the next
+      if (refill == 1) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, cur, j, fs);
       else if (refill == 2) issue_tile<BM, BN, BK, WGM, WGN, NST, WT, 1>(p, nxt, j - nk, fs);
       ++gt;
     }
