@@ -22,19 +22,38 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
 
-// NVFP4 element: E2M1 code (4 bits) -> fp32, from the format's fields.
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const uint32_t mag = c & 7u;
-  uint32_t bits;
-  if (mag < 2u) bits = mag ? 0x3F000000u : 0u;            // 0, 0.5 (subnormal)
-  else bits = (((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22);
-  return __uint_as_float(bits | ((c & 8u) << 28));
+// NVFP4 decode.  A block scale s (E4M3) is converted exactly to fp32 by the
+// hardware (v_cvt_scalef32_f32_fp8, unit scale).  The gfx950 conversion
+// v_cvt_scalef32_pk_f32_fp4 turns one byte (two E2M1 codes, low nibble first)
+// into two fp32 values multiplied by the power of two of its scale operand
+// (only the operand's exponent is used); given |s| it applies
+// 2^floor(log2|s|), and one fp32 multiply by frexp_mant(s) = s / 2^(floor+1)
+// (in [0.5, 1) with s's sign, 0 when s = 0) completes the product.  The result
+// is w / 2 for the element's true value w = e2m1 * s: exact, since every
+// e2m1 * e4m3 product has at most 6 significant bits; the factor 2 is folded
+// into the epilogue's fp32 scale.  The pair is packed to bf16 by taking the
+// high halves (exact values, so truncation is exact).
+struct Fp4Scale {
+  float pow2, frac;
+};
+// byte 0 of `sbyte` is the E4M3 scale
+__device__ __forceinline__ Fp4Scale split_scale(uint32_t sbyte) {
+  const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sbyte, 1.0f, 0);
+  Fp4Scale r;
+  r.pow2 = __builtin_fabsf(s);
+  r.frac = __builtin_amdgcn_frexp_mantf(s);
+  return r;
 }
-// NVFP4 block scale: E4M3 byte -> fp32 (bias 7; exponent field 0 is subnormal).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * (1.0f / 512.0f);
-  return (b & 0x80u) ? -v : v;
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, const Fp4Scale& sc) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc.pow2, BYTE);
+  const float lo = v.x * sc.frac, hi = v.y * sc.frac;
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+// 8 codes (one dword) -> 8 bf16 (one uint4), each half its true value
+__device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
+  return make_uint4(fp4_pair<0>(w, sc), fp4_pair<1>(w, sc), fp4_pair<2>(w, sc), fp4_pair<3>(w, sc));
 }
 
 // OCP FP8 E4M3 quantisation: code = RNE_e4m3(clamp(v * r, -448, 448)), r the
@@ -65,6 +84,9 @@ __device__ __forceinline__ uint4 e4m3x8_bf(uint32_t lo, uint32_t hi) {
 // ------------------------------------------------------------------ kernel params
 // Weight (B operand) storage of a GEMM.  FP8: A and B are both E4M3 codes.
 enum WType : int { WT_BF16 = 0, WT_NVFP4 = 1, WT_FP8 = 2 };
+// the epilogue factor that undoes the halving of decoded NVFP4 weights
+template <int WT>
+constexpr float decode_factor() { return WT == WT_NVFP4 ? 2.0f : 1.0f; }
 
 enum Epi : int {
   EPI_BF16 = 0,        // C(bf16) = g*acc                             (expert down, dense)

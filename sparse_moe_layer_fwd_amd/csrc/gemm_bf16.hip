@@ -100,43 +100,6 @@ __device__ __forceinline__ int swz_chunk(int row, int c) {
   return c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1));
 }
 
-// NVFP4 decode.  A block scale s (E4M3) is converted exactly to fp32 by the
-// hardware (v_cvt_scalef32_f32_fp8, unit scale).  The gfx950 conversion
-// v_cvt_scalef32_pk_f32_fp4 turns one byte (two E2M1 codes, low nibble first)
-// into two fp32 values multiplied by the power of two of its scale operand
-// (only the operand's exponent is used); given |s| it applies
-// 2^floor(log2|s|), and one fp32 multiply by frexp_mant(s) = s / 2^(floor+1)
-// (in [0.5, 1) with s's sign, 0 when s = 0) completes the product.  The result
-// is w / 2 for the element's true value w = e2m1 * s: exact, since every
-// e2m1 * e4m3 product has at most 6 significant bits; the factor 2 is folded
-// into the epilogue's fp32 scale.  The pair is packed to bf16 by taking the
-// high halves (exact values, so truncation is exact).
-struct Fp4Scale {
-  float pow2, frac;
-};
-// byte 0 of `sbyte` is the E4M3 scale
-__device__ __forceinline__ Fp4Scale split_scale(uint32_t sbyte) {
-  const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sbyte, 1.0f, 0);
-  Fp4Scale r;
-  r.pow2 = __builtin_fabsf(s);
-  r.frac = __builtin_amdgcn_frexp_mantf(s);
-  return r;
-}
-template <int BYTE>
-__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, const Fp4Scale& sc) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc.pow2, BYTE);
-  const float lo = v.x * sc.frac, hi = v.y * sc.frac;
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-// 8 codes (one dword) -> 8 bf16 (one uint4), each half its true value
-__device__ __forceinline__ uint4 fp4x8(uint32_t w, const Fp4Scale& sc) {
-  return make_uint4(fp4_pair<0>(w, sc), fp4_pair<1>(w, sc), fp4_pair<2>(w, sc), fp4_pair<3>(w, sc));
-}
-// the epilogue factor that undoes the halving of decoded NVFP4 weights
-template <int WT>
-constexpr float decode_factor() { return WT == WT_NVFP4 ? 2.0f : 1.0f; }
-
 // NVFP4 codes of a 64-deep k-slab in a stage: row r's 32 bytes as two
 // 16-byte halves (the k-tiled layout puts the codes of k 16i + 8h .. + 7, i =
 // 0..3, in half h); half h sits in slot h ^ fp4_slot_swz(r), so that the

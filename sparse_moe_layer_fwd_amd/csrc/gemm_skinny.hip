@@ -21,14 +21,6 @@
 
 namespace moe {
 
-namespace {
-__device__ __forceinline__ uint32_t fp4x2_bf(uint32_t byte, float s) {
-  const float lo = e2m1_to_f32(byte & 15u) * s;
-  const float hi = e2m1_to_f32((byte >> 4) & 15u) * s;
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-}
-}  // namespace
-
 // Rows [row0, row0 + cnt) (cnt <= 64) of expert e, columns [n0, n0 + 64).
 // K range [kbeg, kbeg + klen) (klen a multiple of 256, of 512 when WIDE): each
 // wavefront takes a quarter.  A lane takes 8 * NCH consecutive elements of its
@@ -92,16 +84,16 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
     for (int cb = 0; cb < 4; ++cb) {
       if (FP4) {
         // the step's 64 k are one k-slab: the lane's 16 codes (dwords 2 grp and
-        // 2 grp + 1 of the row, stored at positions grp and 4 + grp) and their scale
+        // 2 grp + 1 of the row, stored at positions grp and 4 + grp) and their
+        // scale, decoded by the hardware conversions to half their value (see
+        // split_scale; the epilogue scale carries the factor 2)
         const int64_t slab = kb / 64;
         const uint8_t* bs = brow[cb] + slab * p.ldb + grp * 4;
         const uint2 c = make_uint2(*reinterpret_cast<const uint32_t*>(bs),
                                    *reinterpret_cast<const uint32_t*>(bs + 16));
-        const float s = e4m3_to_f32(srow[cb][slab * p.lds_scale + grp]);
-        b[cb][0] = make_uint4(fp4x2_bf(c.x & 0xFFu, s), fp4x2_bf((c.x >> 8) & 0xFFu, s),
-                              fp4x2_bf((c.x >> 16) & 0xFFu, s), fp4x2_bf(c.x >> 24, s));
-        b[cb][1] = make_uint4(fp4x2_bf(c.y & 0xFFu, s), fp4x2_bf((c.y >> 8) & 0xFFu, s),
-                              fp4x2_bf((c.y >> 16) & 0xFFu, s), fp4x2_bf(c.y >> 24, s));
+        const Fp4Scale sc = split_scale(srow[cb][slab * p.lds_scale + grp]);
+        b[cb][0] = fp4x8(c.x, sc);
+        b[cb][1] = fp4x8(c.y, sc);
       } else if (FP8 && WIDE) {
 #pragma unroll
         for (int h = 0; h < NCH / 2; ++h) braw[cb][h] = *reinterpret_cast<const uint4*>(brow[cb] + k + 16 * h);
@@ -165,8 +157,10 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
   }
   __syncthreads();
   if (wave != 0) return;                                // the caller re-syncs every wavefront
-  // weight scale times activation scale (1 for bf16 operands)
-  const float sc = (p.b_gscale ? p.b_gscale[e] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f);
+  // weight scale times activation scale (1 for bf16 operands), times 2 for
+  // NVFP4 weights decoded as half their value
+  const float sc = (p.b_gscale ? p.b_gscale[e] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f) *
+                   decode_factor<WT>();
   const float rq = EPI == EPI_SQRELU_Q8 ? 1.0f / *p.q_scale : 1.0f;
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {

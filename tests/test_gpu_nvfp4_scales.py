@@ -2,11 +2,11 @@
 
 NVFP4 weights are E2M1 elements with one E4M3 scale per 16-element block and an
 FP32 global scale ("NVIDIA Nemotron 3: Efficient and Open Intelligence" Korean
-summary, section 2.4 NVFP4 Training).  The kernels decode them in registers:
-the tiled GEMM through the hardware's scaled FP4 conversion (which applies the
-scale's power of two) and one fp32 multiply by the remaining significand, the
-skinny kernel with fp32 products truncated to bf16.  Both claim exactness for
-every finite scale.  Here every one of the 254 finite E4M3 bytes (both signs,
+summary, section 2.4 NVFP4 Training).  The kernels decode them in registers,
+the tiled GEMM and the skinny kernel alike, through the hardware's scaled FP4
+conversion (which applies the scale's power of two) and one fp32 multiply by
+the remaining significand, to half the element's value.  They claim exactness
+for every finite scale.  Here every one of the 254 finite E4M3 bytes (both signs,
 0x00 and 0x80, the subnormals 0x01-0x07, up to 0x7E = 448) is used: expert e's
 W1 and W2 carry scale byte FINITE[e] in every block, each block holds all 16
 E2M1 codes once (a seeded permutation), and the global scale is 1.  Routing
