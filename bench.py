@@ -8,6 +8,7 @@ GEMMs, combine and up-projection, all in libmoe.so on HBM-resident inputs.
     python bench.py [--config 5] [--steps 20] [--warmup 5] [--gpus 1]
     python bench.py --paired      # standard vs latent at the ablation shapes
     python bench.py --paired router_at_d   # router on the latent vs on x at d
+    python bench.py --config 5 --hipblaslt  # torch's bf16 GEMM on the layer's shapes
 
 Prints one JSON line.  `value` is tokens/s of the whole layer.  `roofline`
 describes the dominant kernel (the grouped expert GEMMs): its algorithmic
@@ -175,6 +176,43 @@ class GpuTelemetry:
         return r
 
 
+def hipblaslt_context(cfg, steps, warmup):
+    """torch.nn.functional.linear in bf16 (hipBLASLt on ROCm) on the layer's
+    dense shapes: the two latent projections and one dense GEMM with the FLOPs
+    of a grouped expert launch (T*K rows, l -> m).  Random bf16 operands, fp32
+    accumulation; context for the library's own kernels, not part of the layer."""
+    import torch
+    import torch.nn.functional as F
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    shapes = {}
+    if cfg.latent != cfg.d:
+        shapes["down_proj"] = (cfg.T, cfg.latent, cfg.d)     # rows, out, in
+        shapes["up_proj"] = (cfg.T, cfg.d, cfg.latent)
+    shapes["expert_up_as_dense"] = (cfg.T * cfg.top_k, cfg.ffn, cfg.latent)
+    out = {"what": "torch bf16 linear (hipBLASLt) on %s shapes" % cfg.name, "steps": steps}
+    for name, (m, n, k) in shapes.items():
+        a = torch.randn((m, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        w = (torch.randn((n, k), generator=g, device=dev, dtype=torch.float32) / k ** 0.5).to(torch.bfloat16)
+        for _ in range(warmup):
+            F.linear(a, w)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            F.linear(a, w)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out[name] = {"m_n_k": [m, n, k], "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, w
+        torch.cuda.empty_cache()
+    return out
+
+
 def forced_workload(cfg, seed):
     """The layer's workload with every token routed to the same K experts
     (experts 0, N/K, 2N/K, ...: a large router bias on them): every expert GEMM
@@ -238,6 +276,19 @@ def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=Fals
     step_stats = {"median": round(per_step[len(per_step) // 2], 5), "min": round(per_step[0], 5),
                   "max": round(per_step[-1], 5)}
     log("bench: %.3f ms/step (median %.3f)" % (ms_step, step_stats["median"]))
+    # the grouped expert GEMMs' two phases (full row tiles, remainder tiles),
+    # timed as separate launches over further steps after the timed region
+    B.moe_profile_enable(2)
+    for _ in range(steps):
+        layer.forward(x, ws=ws, y=y)
+    torch.cuda.synchronize()
+    B.moe_profile_enable(False)
+    split = B.moe_profile_read()
+    phases = None
+    if split["expert_up_rem"][0]:
+        phases = {"steps": steps}
+        phases.update({k: round(split[k][1] / steps, 5) for k in
+                       ("expert_up", "expert_up_rem", "expert_down", "expert_down_rem")})
     # clock and power under the same load: sampled over further steps (at
     # least telemetry_ms) after the timed region, which stays untouched
     telemetry = None
@@ -252,7 +303,8 @@ def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=Fals
     del layer, ws, x, y
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
-            "touched": int((counts_np > 0).sum()), "telemetry": telemetry, "step_stats": step_stats}
+            "touched": int((counts_np > 0).sum()), "telemetry": telemetry, "step_stats": step_stats,
+            "phases": phases}
 
 
 # Paired comparisons: (metric, (role a, role b), [(regime, config of a, config of b)])
@@ -330,6 +382,8 @@ def main():
                     help="ablation: the chosen layer with its routed experts in another storage type")
     ap.add_argument("--forced-routing", action="store_true",
                     help="ablation: every token routed to the same K experts (full row tiles only)")
+    ap.add_argument("--hipblaslt", action="store_true",
+                    help="context only: time torch's bf16 GEMM (hipBLASLt) on the layer's dense shapes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
@@ -359,6 +413,9 @@ def main():
 
     from sparse_moe_layer_fwd_amd.workloads import CONFIGS
 
+    if args.hipblaslt:
+        print(json.dumps(hipblaslt_context(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return
     if args.paired:
         paired(args)
         return
@@ -427,6 +484,9 @@ def main():
         # decode-regime figure
         "layer_hbm_frac": round(layer_bytes(cfg, touched) / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "stages_ms_per_step": {k: round(v[1] / max(1, args.steps), 5) for k, v in stages.items() if v[0]},
+        # the grouped GEMMs split into their full-tile and remainder-tile
+        # launches (ms per step; further steps after the timed region)
+        "grouped_gemm_phases_ms_per_step": r["phases"],
         # graphics clock and socket power, sampled over further steps of the
         # same workload right after the timed region
         "gpu_telemetry": r["telemetry"],

@@ -201,17 +201,25 @@ const char* moe_status_string(int status);
  * EXPERT_UP).  EXPERT_UP and EXPERT_DOWN are the two
  * grouped expert GEMMs; SHARED covers both shared-expert GEMMs (and the FP8
  * quantisation of their input); QUANT is the FP8 quantisation of x for FP8
- * routed experts of a layer without latent projection. */
+ * routed experts of a layer without latent projection.  EXPERT_UP_REM and
+ * EXPERT_DOWN_REM are recorded only in the phase-split mode below. */
 enum moe_stage {
   MOE_STAGE_DOWN_PROJ = 0, MOE_STAGE_ROUTER, MOE_STAGE_TOPK, MOE_STAGE_SCAN,
   MOE_STAGE_SCATTER, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_SHARED,
-  MOE_STAGE_COMBINE, MOE_STAGE_UP_PROJ, MOE_STAGE_QUANT, MOE_NUM_STAGES
+  MOE_STAGE_COMBINE, MOE_STAGE_UP_PROJ, MOE_STAGE_QUANT, MOE_STAGE_EXPERT_UP_REM,
+  MOE_STAGE_EXPERT_DOWN_REM, MOE_NUM_STAGES
 };
 
 /* enable = 1: later moe_route / moe_forward calls record a HIP event pair
  * around each stage on the caller's stream (process-wide setting; the events
- * are host-side objects, no device memory is allocated).  enable = 0 stops
- * recording.  Returns MOE_OK, or MOE_ERR_HIP if an event cannot be created. */
+ * are host-side objects, no device memory is allocated).  enable = 2 also
+ * splits each tiled grouped expert GEMM into two launches of the same kernel,
+ * the full row tiles (timed as EXPERT_UP / EXPERT_DOWN) and then the
+ * remainder tiles of each expert's last rows (EXPERT_UP_REM /
+ * EXPERT_DOWN_REM): a measurement mode with the same results, a few percent
+ * slower than the single launch.  enable = 0 stops recording.  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG for another value, or MOE_ERR_HIP if an event cannot be
+ * created. */
 int moe_profile_enable(int enable);
 
 /* Waits for every recorded event, then writes per stage the number of

@@ -20,7 +20,7 @@ EXPORTED = ("moe_init", "moe_workspace_size", "moe_route", "moe_forward", "moe_f
             "moe_quantize_fp8", "moe_nvfp4_tile",
             "moe_destroy", "moe_status_string", "moe_profile_enable", "moe_profile_read",
             "moe_stage_name")
-MOE_NUM_STAGES = 11
+MOE_NUM_STAGES = 13
 
 
 class MoEConfig(ctypes.Structure):
@@ -158,8 +158,9 @@ def moe_destroy(h) -> int:
     return lib().moe_destroy(h)
 
 
-def moe_profile_enable(enable: bool) -> int:
-    st = lib().moe_profile_enable(1 if enable else 0)
+def moe_profile_enable(enable) -> int:
+    """False / True, or 2: the phase-split timing mode (include/moe.h)."""
+    st = lib().moe_profile_enable(int(enable))
     _check(st, "moe_profile_enable")
     return st
 

@@ -122,6 +122,7 @@ struct GemmArgs {
   int32_t M, N, K;
   const int4* tiles; const int* n_tiles;              // grouped: (group, row0, row1, -)
   const int4* tiles2;                                 // grouped: second (remainder) list
+  int32_t lists;                                      // grouped: bit 0 list 0, bit 1 list 1
   void* C; int64_t ldc; void* C2; int64_t ldc2;
   const float* bias;                                  // per column
   const float* add; int64_t ld_add;                   // fp32 addend

@@ -1009,7 +1009,8 @@ __device__ __forceinline__ void gemm_stream_lean(const GemmArgs& p, char* smem, 
 
 // Persistent kernel.  Phase 1 walks list 0 (row tiles of height <= BM, or the
 // dense row blocks), phase 2 list 1 (row tiles of height <= BMS: the remainder
-// of each expert's rows) with its own ring.  Block b takes the
+// of each expert's rows) with its own ring; p.lists selects the lists of a
+// grouped launch (both, or one for a timing run per phase).  Block b takes the
 // items of its XCD's slice of each round of gridDim.x items (block b runs on
 // XCD b % 8), so consecutive items (the column tiles of one row tile, then the
 // next row tiles of the same expert) share an L2.
@@ -1020,25 +1021,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   char* smem = reinterpret_cast<char*>(smem_u4);
   const int G = gridDim.x;
   const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int nrt0 = p.tiles ? p.n_tiles[0] : (p.M + BM - 1) / BM;
+  const int nrt0 = !p.tiles ? (p.M + BM - 1) / BM : (p.lists & 1) ? p.n_tiles[0] : 0;
+  const int nrt1 = p.tiles && (p.lists & 2) ? p.n_tiles[1] : 0;
   if constexpr (WT != WT_NVFP4 && WGM * WGN == 8 && BK1 == 64 && BK2 == 64 && BMS > 0) {
     if (p.K >= 3 * BK1) {                    // three B stages of one tile
       gemm_stream_ab<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
       if constexpr (BMS > 0)
-        gemm_stream_ab<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+        gemm_stream_ab<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, nrt1, base, G);
     } else {
       gemm_stream_lean<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
       if constexpr (BMS > 0)
-        gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+        gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, nrt1, base, G);
     }
   } else if constexpr (WT != WT_NVFP4) {
     gemm_stream_lean<BM, BN, BK1, WGM, WGN, NST1, WT, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
-      gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+      gemm_stream_lean<BMS, BN, BK2, WGM, WGN, NST2, WT, EPI>(p, smem, p.tiles2, nrt1, base, G);
   } else {
     gemm_stream_fp4<BM, BN, BK1, WGM, WGN, NST1, EPI>(p, smem, p.tiles, nrt0, base, G);
     if constexpr (BMS > 0)
-      gemm_stream_fp4<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+      gemm_stream_fp4<BMS, BN, BK2, WGM, WGN, NST2, EPI>(p, smem, p.tiles2, nrt1, base, G);
   }
 }
 

@@ -57,6 +57,7 @@ thread_local bool tls_no_stage_events = false;
 struct Prof {
   std::mutex mu;
   bool on = false;
+  bool split = false;        // grouped expert GEMMs as two launches, one per tile list
   struct Rec { int stage; hipEvent_t a, b; };
   std::vector<Rec> pending;
   std::vector<hipEvent_t> pool;
@@ -77,6 +78,13 @@ hipEvent_t prof_event() {
   hipEvent_t e = nullptr;
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
+}
+// The phase-split timing mode (moe_profile_enable(2)) is on.
+bool prof_split() {
+  if (tls_no_stage_events) return false;
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  return P.on && P.split;
 }
 // Records the start of a stage; returns the index of its record or -1.
 int prof_begin(int stage, hipStream_t s) {
@@ -105,6 +113,10 @@ struct StageScope {
   hipStream_t s;
   StageScope(int stage, hipStream_t st) : rec(prof_begin(stage, st)), s(st) {}
   ~StageScope() { prof_end(rec, s); }
+  void end() {   // ends the stage before the scope does
+    prof_end(rec, s);
+    rec = -1;
+  }
 };
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -278,6 +290,7 @@ GemmArgs gemm_args() {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.kseg = 1 << 30;
+  a.lists = 3;
   return a;
 }
 
@@ -425,6 +438,17 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   const int bn = p.bm == 256 ? 256 : 128;
   const int64_t ntn = (rows + bn - 1) / bn;
   const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
+  if (p.bms > 0 && prof_split()) {
+    // phase-split timing: the full row tiles, then the remainder tiles, as
+    // two launches of the same kernel (same results)
+    a.lists = 1;
+    MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+    sc.end();
+    StageScope rem(up ? MOE_STAGE_EXPERT_UP_REM : MOE_STAGE_EXPERT_DOWN_REM, s);
+    a.lists = 2;
+    MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+    return MOE_OK;
+  }
   MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
   return MOE_OK;
 }
@@ -544,9 +568,11 @@ int moe_workspace_size(moe_handle_t h, int32_t T, size_t* bytes) {
 }
 
 int moe_profile_enable(int enable) {
+  if (enable < 0 || enable > 2) return MOE_ERR_INVALID_ARG;
   Prof& P = prof();
   std::lock_guard<std::mutex> g(P.mu);
   P.on = enable != 0;
+  P.split = enable == 2;
   return MOE_OK;
 }
 
@@ -578,7 +604,7 @@ int moe_profile_read(int32_t* launches, double* ms) {
 const char* moe_stage_name(int stage) {
   static const char* names[MOE_NUM_STAGES] = {"down_proj", "router", "topk", "scan", "scatter",
                                               "expert_up", "expert_down", "shared", "combine",
-                                              "up_proj", "quant_x"};
+                                              "up_proj", "quant_x", "expert_up_rem", "expert_down_rem"};
   return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "unknown";
 }
 
