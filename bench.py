@@ -74,28 +74,92 @@ def layer_bytes(cfg, touched):
     return b
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the grouped expert GEMM from the committed counter
-    summary (FETCH_SIZE, WRITE_SIZE scaled by a plain-copy calibration), or None
-    when the kernel sources changed since the counters were taken."""
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def source_sha256():
+    """Hash of the kernel sources (csrc/*), which the counter summary is tied to."""
     import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
     h = hashlib.sha256()
     for src in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_fwd_amd", "csrc", "*"))):
         with open(src, "rb") as f:
             h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the grouped expert GEMM from the committed counter
+    summary (FETCH_SIZE, WRITE_SIZE scaled by a plain-copy calibration), or None
+    when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as f:
+        rec = json.load(f)
     w = rec.get("workloads", {}).get(workload)
-    if h.hexdigest() != rec.get("source_sha256") or not w:
+    if source_sha256() != rec.get("source_sha256") or not w:
         return None
     if w.get("fetch_kib_per_dispatch") is None or w.get("write_kib_per_dispatch") is None:
         return None
     return (w["fetch_kib_per_dispatch"] * rec["fetch_scale"] +
             w["write_kib_per_dispatch"] * rec["write_scale"]) * 1024.0
+
+
+def is_grouped_expert_kernel(name):
+    """The grouped expert GEMMs: the tiled kernel with a remainder list (its
+    third template argument, the remainder tile height, is nonzero; the dense
+    projections have 0) or the skinny expert kernel."""
+    import re
+    m = re.search(r"gemm_bf16_kernel<\s*\d+,\s*\d+,\s*(\d+),", name)
+    return bool(m and int(m.group(1)) > 0) or "skinny_kernel<" in name
+
+
+def traffic_summary(indir, config_ids):
+    """Summarise rocprofv3 --pmc runs into profiles/traffic_counters.json:
+    indir/fetch<N> and indir/write<N> hold the FETCH_SIZE and WRITE_SIZE runs
+    of `bench.py --config N`, indir/copy_fetch and indir/copy_write those of
+    `bench.py --copy-calibration 1024`.  Per workload, the counters of the
+    grouped expert GEMM dispatches are averaged (KiB per dispatch); the copy
+    gives the factor from each counter to HBM bytes.  Prints a markdown table."""
+    import csv
+    import glob
+    from sparse_moe_layer_fwd_amd.workloads import CONFIGS
+
+    def dispatches(sub, counter):
+        per = {}
+        for path in glob.glob(os.path.join(indir, sub, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row["Counter_Name"] != counter:
+                        continue
+                    key = (path, row["Dispatch_Id"])
+                    rec = per.setdefault(key, [row["Kernel_Name"], 0.0])
+                    rec[1] += float(row["Counter_Value"])
+        return list(per.values())
+
+    copy_kib = 1024.0 * 1024.0                  # the 1 GiB copy, in KiB
+    fetch_copy = max(v for _, v in dispatches("copy_fetch", "FETCH_SIZE"))
+    write_copy = max(v for _, v in dispatches("copy_write", "WRITE_SIZE"))
+    out = {"source_sha256": source_sha256(), "fetch_scale": round(copy_kib / fetch_copy, 4),
+           "write_scale": round(copy_kib / write_copy, 4), "workloads": {}}
+    rows = ["| workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | write GB | traffic GB / launch |",
+            "|---|---|---|---|---|---|---|"]
+    for cid in config_ids:
+        cfg = CONFIGS[cid]
+        f = [(k, v) for k, v in dispatches("fetch%d" % cid, "FETCH_SIZE") if is_grouped_expert_kernel(k)]
+        w = [(k, v) for k, v in dispatches("write%d" % cid, "WRITE_SIZE") if is_grouped_expert_kernel(k)]
+        if not f or not w:
+            continue
+        fk, wk = sum(v for _, v in f) / len(f), sum(v for _, v in w) / len(w)
+        out["workloads"][cfg.name] = {"kernel": " | ".join(sorted({k for k, _ in f})), "dispatches": len(f),
+                                      "fetch_kib_per_dispatch": round(fk), "write_kib_per_dispatch": round(wk)}
+        rd, wr = fk * out["fetch_scale"] * 1024 / 1e9, wk * out["write_scale"] * 1024 / 1e9
+        rows.append("| %s | %d | %d | %d | %.3f | %.3f | %.3f |" % (cfg.name, len(f), fk, wk, rd, wr, rd + wr))
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print("calibration: FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB per 1 GiB copy" % (fetch_copy, write_copy))
+    print("\n".join(rows))
 
 
 def cpu_baseline(cfg, seed, sample):
@@ -229,7 +293,7 @@ def forced_workload(cfg, seed):
     return Forced(cfg, seed)
 
 
-def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=False):
+def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=False, phases=True):
     """Build the layer with seeded weights, warm up, then time `steps`
     back-to-back moe_forward calls on the current stream (inputs resident in
     HBM) with the library's per-stage timer on."""
@@ -278,17 +342,18 @@ def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=Fals
     log("bench: %.3f ms/step (median %.3f)" % (ms_step, step_stats["median"]))
     # the grouped expert GEMMs' two phases (full row tiles, remainder tiles),
     # timed as separate launches over further steps after the timed region
-    B.moe_profile_enable(2)
-    for _ in range(steps):
-        layer.forward(x, ws=ws, y=y)
-    torch.cuda.synchronize()
-    B.moe_profile_enable(False)
-    split = B.moe_profile_read()
-    phases = None
-    if split["expert_up_rem"][0]:
-        phases = {"steps": steps}
-        phases.update({k: round(split[k][1] / steps, 5) for k in
-                       ("expert_up", "expert_up_rem", "expert_down", "expert_down_rem")})
+    split_ms = None
+    if phases:
+        B.moe_profile_enable(2)
+        for _ in range(steps):
+            layer.forward(x, ws=ws, y=y)
+        torch.cuda.synchronize()
+        B.moe_profile_enable(False)
+        split = B.moe_profile_read()
+        if split["expert_up_rem"][0]:
+            split_ms = {"steps": steps}
+            split_ms.update({k: round(split[k][1] / steps, 5) for k in
+                             ("expert_up", "expert_up_rem", "expert_down", "expert_down_rem")})
     # clock and power under the same load: sampled over further steps (at
     # least telemetry_ms) after the timed region, which stays untouched
     telemetry = None
@@ -304,7 +369,7 @@ def time_layer(cfg, cfg_id, seed, steps, warmup, telemetry_ms=500.0, forced=Fals
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "stages": stages, "counts": counts_np,
             "touched": int((counts_np > 0).sum()), "telemetry": telemetry, "step_stats": step_stats,
-            "phases": phases}
+            "phases": split_ms}
 
 
 # Paired comparisons: (metric, (role a, role b), [(regime, config of a, config of b)])
@@ -337,7 +402,7 @@ def paired(args):
         rec = {"regime": regime}
         for role, cid in ((ra, a_id), (rb, b_id)):
             cfg = CONFIGS[cid]
-            r = time_layer(cfg, cid, args.seed, args.steps, args.warmup)
+            r = time_layer(cfg, cid, args.seed, args.steps, args.warmup, phases=False)
             rec[role] = {
                 "workload": cfg.name, "T": cfg.T, "d": cfg.d, "latent": cfg.latent,
                 "n_experts": cfg.n_experts, "top_k": cfg.top_k, "ffn": cfg.ffn,
@@ -384,9 +449,17 @@ def main():
                     help="ablation: every token routed to the same K experts (full row tiles only)")
     ap.add_argument("--hipblaslt", action="store_true",
                     help="context only: time torch's bf16 GEMM (hipBLASLt) on the layer's dense shapes")
+    ap.add_argument("--no-phases", action="store_true",
+                    help="skip the phase-split steps after the timed region (for profiler runs)")
+    ap.add_argument("--traffic-summary", metavar="DIR", default=None,
+                    help="write profiles/traffic_counters.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs "
+                         "under DIR (fetch<N>, write<N>, copy_fetch, copy_write); no GPU needed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scales HBM traffic counters)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, [2, 3, 4, 5, 11, 12, 13])
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: it measures the layer on a single MI355X "
@@ -426,7 +499,7 @@ def main():
     if args.forced_routing:
         cfg = cfg.replace(name=cfg.name + "+forced_routing")
     r = time_layer(cfg, args.config, args.seed, args.steps, args.warmup, args.telemetry_ms,
-                   forced=args.forced_routing)
+                   forced=args.forced_routing, phases=not args.no_phases)
     ms_step, stages, counts_np, touched = r["ms_step"], r["stages"], r["counts"], r["touched"]
 
     # dominant kernel: the grouped expert GEMMs (two launches per step)
