@@ -26,9 +26,11 @@ namespace moe {
 // wavefront takes a quarter.  A lane takes 8 * NCH consecutive elements of its
 // rows per step: 16, or 32 E4M3 codes when WIDE (FP8 only), so an FP8 step
 // loads as many bytes per lane as a bf16 one.
+// sc: the output scale, rq: the reciprocal quantisation scale (EPI_SQRELU_Q8).
 template <int WT, int EPI, bool WIDE = false>
 __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[16][4][64], int e,
-                                             int row0, int cnt, int n0, int kbeg, int klen) {
+                                             int row0, int cnt, int n0, int kbeg, int klen,
+                                             float sc = 1.0f, float rq = 1.0f) {
   constexpr bool FP4 = WT == WT_NVFP4, FP8 = WT == WT_FP8;
   static_assert(!WIDE || FP8, "32-element steps for FP8 codes");
   constexpr int NCH = WIDE ? 4 : 2;                      // 8-element chunks per lane and step
@@ -157,11 +159,6 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
   }
   __syncthreads();
   if (wave != 0) return;                                // the caller re-syncs every wavefront
-  // weight scale times activation scale (1 for bf16 operands), times 2 for
-  // NVFP4 weights decoded as half their value
-  const float sc = (p.b_gscale ? p.b_gscale[e] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f) *
-                   decode_factor<WT>();
-  const float rq = EPI == EPI_SQRELU_Q8 ? 1.0f / *p.q_scale : 1.0f;
 #pragma unroll
   for (int rb = 0; rb < MAXRB; ++rb) {
     if (rb >= nrb) continue;
@@ -207,8 +204,14 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
   const int cnt = p.counts[e];
   if (cnt == 0) return;
   const int row0 = p.offs[e];
+  // weight scale times activation scale (1 for bf16 operands), times 2 for
+  // NVFP4 weights decoded as half their value; loaded here, ahead of the
+  // weight stream, so the epilogue does not wait for them
+  const float sc = (p.b_gscale ? p.b_gscale[e] : 1.0f) * (p.a_scale ? *p.a_scale : 1.0f) *
+                   decode_factor<WT>();
+  const float rq = EPI == EPI_SQRELU_Q8 ? 1.0f / *p.q_scale : 1.0f;
   for (int c0 = 0; c0 < cnt; c0 += 64) {
-    skinny_chunk<WT, EPI, WIDE>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K);
+    skinny_chunk<WT, EPI, WIDE>(p, red, e, row0 + c0, min(64, cnt - c0), blockIdx.x * 64, 0, p.K, sc, rq);
     __syncthreads();
   }
 }
