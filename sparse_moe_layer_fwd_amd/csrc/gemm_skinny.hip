@@ -195,10 +195,21 @@ __device__ __forceinline__ void skinny_chunk(const SkinnyArgs& p, float (*red)[1
   }
 }
 
+// Wavefronts per SIMD the register allocation must allow.  Left to itself the
+// compiler gives these kernels 220-240 registers per lane (64 of them AGPRs),
+// two wavefronts per SIMD; capped at 168 (no spills), three blocks share a CU.  That
+// pays where a weight element costs decode work between its load and its MFMA
+// (E4M3 and NVFP4 codes: FP8 decode expert GEMMs 0.381 -> 0.326 ms, NVFP4
+// 0.629 -> 0.596 ms on the Ultra-like decode shape); bf16 weights stream
+// slightly faster (1%) with the larger allocation.
+template <int WT>
+constexpr int skinny_waves() { return WT == WT_BF16 ? 1 : 3; }
+
 // Grid (column tiles of 64, experts).  Each expert's rows are processed in
 // chunks of up to 64 rows.
 template <int WT, int EPI, bool WIDE = false>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(skinny_waves<WT>())))
+void skinny_kernel(SkinnyArgs p) {
   __shared__ float red[3][16][4][64];                    // partial sums of waves 1..3
   const int e = blockIdx.y;
   const int cnt = p.counts[e];
@@ -219,8 +230,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs p) {
 // Dense split-K: grid (N / 64, ks, row chunks of 64).  Block (x, y, z) sums
 // rows [64 z, 64 z + 64) x columns [64 x, 64 x + 64) over K slice y into the
 // fp32 partials P[y].
+// (three wavefronts per SIMD here for every operand type: the split-K
+// projections measured 2-3% faster with them)
 template <int WT, bool WIDE = false>
-__global__ __launch_bounds__(256) void skinny_dense_kernel(SkinnyArgs p, int M) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void skinny_dense_kernel(SkinnyArgs p, int M) {
   __shared__ float red[3][16][4][64];
   const int kl = p.K / (int)gridDim.y;
   const int row0 = blockIdx.z * 64;
