@@ -126,6 +126,14 @@ SMALL = {
                                 ffn=1024),
     "multi_item_nvfp4": MoEConfig("multi_item_nvfp4", T=8192, d=256, latent=256, n_experts=8,
                                   top_k=4, ffn=1024, expert="nvfp4", zipf_s=1.1),
+    # bf16 experts of 128-255 rows on average: remainders of up to 192 rows on
+    # 192-row tiles, longer ones on a partial 256-row tile (uniform routing:
+    # both kinds; Zipf routing: also hot experts with full tiles before them)
+    "mid_tiles_std_shared": MoEConfig("mid_tiles_std_shared", T=1000, d=256, latent=256,
+                                      n_experts=32, top_k=6, ffn=256, n_shared=1, shared_ffn=128,
+                                      has_latent_proj=False),
+    "mid_tiles_zipf": MoEConfig("mid_tiles_zipf", T=800, d=256, latent=128, n_experts=16, top_k=4,
+                                ffn=192, zipf_s=1.1),
     # small batches above 64 tokens on the skinny expert kernel: experts with
     # more than 64 rows run it in several 64-row chunks
     "skinny_multi_chunk_bf16": MoEConfig("skinny_multi_chunk_bf16", T=128, d=512, latent=256,
