@@ -230,11 +230,15 @@ class GpuTelemetry:
 
     def record(self):
         r = {"samples": len(self.clk), "period_s": self.period}
+        # instantaneous readings: samples that fall between kernels read idle
+        # clocks, so the median is the figure under load
+        med = lambda v: sorted(v)[len(v) // 2]
         if self.clk:
-            r.update({"sclk_mhz_mean": round(sum(self.clk) / len(self.clk), 1), "sclk_mhz_min": min(self.clk),
-                      "sclk_mhz_max": max(self.clk)})
+            r.update({"sclk_mhz_median": med(self.clk), "sclk_mhz_mean": round(sum(self.clk) / len(self.clk), 1),
+                      "sclk_mhz_min": min(self.clk), "sclk_mhz_max": max(self.clk)})
         if self.pwr:
-            r.update({"power_w_mean": round(sum(self.pwr) / len(self.pwr), 1), "power_w_max": max(self.pwr)})
+            r.update({"power_w_median": med(self.pwr), "power_w_mean": round(sum(self.pwr) / len(self.pwr), 1),
+                      "power_w_max": max(self.pwr)})
         if self.error:
             r["error"] = self.error
         return r
