@@ -161,6 +161,9 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int epi, int ks, const float*
 // leading dimension in elements = bytes, all even)
 hipError_t launch_gemm_bf16(const GemmArgs& a, int wt, int epi, int bm, int bn, int bms,
                             int64_t max_items, int num_cu, hipStream_t s);
+// list 1 (the remainder tiles, height 128) of a grouped NVFP4 GEMM alone, on
+// 4-wavefront 128 x 256 tiles, two blocks per CU; epi EPI_SQRELU_BF16 or EPI_BF16
+hipError_t launch_gemm_fp4_rem(const GemmArgs& a, int epi, int64_t max_items, int num_cu, hipStream_t s);
 hipError_t launch_skinny(const SkinnyArgs& a, int wt, int epi, int n_experts, hipStream_t s);
 // out[i] = E4M3 code of in[i] / *scale (in bf16), n % 16 == 0
 hipError_t launch_quant_fp8(const uint16_t* in, int64_t n, const float* scale, uint8_t* out,

@@ -1044,6 +1044,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs p) {
   }
 }
 
+// The remainder list (list 1) of NVFP4 weights as a launch of its own: 128 x
+// 256 tiles on 4 wavefronts (1 x 4 grid) with two ring stages, two blocks per
+// CU (66 KB of LDS and at most 256 registers each), so every SIMD runs
+// wavefronts of two independent pipelines.  That phase is bound by latency,
+// not by its MFMAs or weight bytes.
+template <int BK, int NST, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_fp4_rem_kernel(GemmArgs p) {
+  extern __shared__ uint4 smem_u4[];
+  char* smem = reinterpret_cast<char*>(smem_u4);
+  const int G = gridDim.x;
+  const int base = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  gemm_stream_fp4<128, 256, BK, 1, 4, NST, EPI>(p, smem, p.tiles2, p.n_tiles[1], base, G);
+}
+
 namespace {
 
 template <int BM, int BN, int BMS, int WGM, int WGN, int BK1, int NST1, int BK2, int NST2, int WT,
@@ -1150,6 +1164,46 @@ hipError_t launch_shape(const GemmArgs& a, int wt, int epi, int64_t grid, int nu
 }
 
 }  // namespace
+
+namespace {
+template <int BK, int EPI>
+hipError_t launch_fp4_rem_one(const GemmArgs& a, int64_t max_items, int num_cu, hipStream_t s) {
+  using C = TileCfg<128, 256, BK, 1, 4, 2, WT_NVFP4>;
+  static_assert(C::LDS <= 80 * 1024, "two blocks per CU");
+  auto* kern = gemm_fp4_rem_kernel<BK, 2, EPI>;
+  if (a.K / BK < 2) return hipErrorInvalidValue;
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_release);
+  }
+  const int64_t cap = ((int64_t)num_cu * 2) & ~7LL;
+  int grid = (int)(max_items < cap ? max_items : cap);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), C::LDS, s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_fp4_rem(const GemmArgs& a, int epi, int64_t max_items, int num_cu, hipStream_t s) {
+  if (!a.tiles2 || !a.n_tiles) return hipErrorInvalidValue;
+  const bool wide = a.K >= 128;
+  switch (epi) {
+    case EPI_SQRELU_BF16:
+      return wide ? launch_fp4_rem_one<64, EPI_SQRELU_BF16>(a, max_items, num_cu, s)
+                  : launch_fp4_rem_one<32, EPI_SQRELU_BF16>(a, max_items, num_cu, s);
+    case EPI_BF16:
+      return wide ? launch_fp4_rem_one<64, EPI_BF16>(a, max_items, num_cu, s)
+                  : launch_fp4_rem_one<32, EPI_BF16>(a, max_items, num_cu, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 // Tile shapes: 256x256 (8 wavefronts, 2x4; 1x8 for grouped NVFP4 weights),
 // 256x128 and 128x128 (4 wavefronts, 2x2).  Dense (a.tiles == nullptr): bms must be 0.  Grouped: list 0 of height

@@ -438,15 +438,24 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   const int bn = p.bm == 256 ? 256 : 128;
   const int64_t ntn = (rows + bn - 1) / bn;
   const int64_t items = (int64_t)(p.max_tiles + p.max_tiles2) * ntn;
-  if (p.bms > 0 && prof_split()) {
-    // phase-split timing: the full row tiles, then the remainder tiles, as
-    // two launches of the same kernel (same results)
+  // NVFP4 weights on the 256-row plan: the remainder tiles get a launch of
+  // their own (two blocks per CU), after the full row tiles
+  const bool fp4_rem = wt == WT_NVFP4 && p.bm == 256 && p.bms == 128;
+  if (p.bms > 0 && (prof_split() || fp4_rem)) {
+    // with phase-split timing the two lists are two launches of the same
+    // kernel otherwise (same results)
     a.lists = 1;
     MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
-    sc.end();
-    StageScope rem(up ? MOE_STAGE_EXPERT_UP_REM : MOE_STAGE_EXPERT_DOWN_REM, s);
     a.lists = 2;
-    MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+    const int64_t items2 = (int64_t)p.max_tiles2 * ntn;
+    if (prof_split()) {
+      sc.end();
+      StageScope rem(up ? MOE_STAGE_EXPERT_UP_REM : MOE_STAGE_EXPERT_DOWN_REM, s);
+      if (fp4_rem) MOE_TRY(launch_gemm_fp4_rem(a, epi, items2, h->num_cu, s));
+      else MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
+    } else {
+      MOE_TRY(launch_gemm_fp4_rem(a, epi, items2, h->num_cu, s));
+    }
     return MOE_OK;
   }
   MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
