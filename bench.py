@@ -52,11 +52,15 @@ def expert_weight_bytes_per_matrix(cfg):
 def expert_kernel(cfg):
     """The kernel the library runs the grouped expert GEMMs on: the skinny
     kernel for batches of up to 128 tokens when l and m are multiples of 256,
-    the tiled MFMA kernel otherwise (fp32 kernel for an all-fp32 layer)."""
+    the tiled MFMA kernel otherwise (fp32 kernel for an all-fp32 layer); with
+    NVFP4 weights on 256-row tiles (64 or more rows per expert on average) the
+    remainder tiles run as a second launch, gemm_fp4_rem_kernel."""
     if cfg.act == "f32":
         return "gemm_f32_kernel"
     if cfg.T <= 128 and cfg.latent % 256 == 0 and cfg.ffn % 256 == 0:
         return "skinny_kernel"
+    if cfg.expert == "nvfp4" and cfg.T * cfg.top_k >= 64 * cfg.n_experts:
+        return "gemm_bf16_kernel + gemm_fp4_rem_kernel"
     return "gemm_bf16_kernel"
 
 
@@ -108,10 +112,11 @@ def measured_traffic(workload):
 def is_grouped_expert_kernel(name):
     """The grouped expert GEMMs: the tiled kernel with a remainder list (its
     third template argument, the remainder tile height, is nonzero; the dense
-    projections have 0) or the skinny expert kernel."""
+    projections have 0), the NVFP4 remainder-tile kernel, or the skinny expert
+    kernel."""
     import re
     m = re.search(r"gemm_bf16_kernel<\s*\d+,\s*\d+,\s*(\d+),", name)
-    return bool(m and int(m.group(1)) > 0) or "skinny_kernel<" in name
+    return bool(m and int(m.group(1)) > 0) or "skinny_kernel<" in name or "gemm_fp4_rem_kernel<" in name
 
 
 def traffic_summary(indir, config_ids):
@@ -150,8 +155,12 @@ def traffic_summary(indir, config_ids):
         w = [(k, v) for k, v in dispatches("write%d" % cid, "WRITE_SIZE") if is_grouped_expert_kernel(k)]
         if not f or not w:
             continue
-        fk, wk = sum(v for _, v in f) / len(f), sum(v for _, v in w) / len(w)
-        out["workloads"][cfg.name] = {"kernel": " | ".join(sorted({k for k, _ in f})), "dispatches": len(f),
+        # per grouped GEMM: every matched dispatch summed, over the GEMM calls
+        # (an NVFP4 GEMM is two launches, its remainder tiles the second)
+        nf = len([k for k, _ in f if "gemm_fp4_rem_kernel<" not in k])
+        nw = len([k for k, _ in w if "gemm_fp4_rem_kernel<" not in k])
+        fk, wk = sum(v for _, v in f) / max(1, nf), sum(v for _, v in w) / max(1, nw)
+        out["workloads"][cfg.name] = {"kernel": " | ".join(sorted({k for k, _ in f})), "dispatches": nf,
                                       "fetch_kib_per_dispatch": round(fk), "write_kib_per_dispatch": round(wk)}
         rd, wr = fk * out["fetch_scale"] * 1024 / 1e9, wk * out["write_scale"] * 1024 / 1e9
         rows.append("| %s | %d | %d | %d | %.3f | %.3f | %.3f |" % (cfg.name, len(f), fk, wk, rd, wr, rd + wr))
