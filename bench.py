@@ -147,7 +147,7 @@ def traffic_summary(indir, config_ids):
     write_copy = max(v for _, v in dispatches("copy_write", "WRITE_SIZE"))
     out = {"source_sha256": source_sha256(), "fetch_scale": round(copy_kib / fetch_copy, 4),
            "write_scale": round(copy_kib / write_copy, 4), "workloads": {}}
-    rows = ["| workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | write GB | traffic GB / launch |",
+    rows = ["| workload | GEMM calls | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | write GB | traffic GB / GEMM |",
             "|---|---|---|---|---|---|---|"]
     for cid in config_ids:
         cfg = CONFIGS[cid]
@@ -163,7 +163,7 @@ def traffic_summary(indir, config_ids):
         out["workloads"][cfg.name] = {"kernel": " | ".join(sorted({k for k, _ in f})), "dispatches": nf,
                                       "fetch_kib_per_dispatch": round(fk), "write_kib_per_dispatch": round(wk)}
         rd, wr = fk * out["fetch_scale"] * 1024 / 1e9, wk * out["write_scale"] * 1024 / 1e9
-        rows.append("| %s | %d | %d | %d | %.3f | %.3f | %.3f |" % (cfg.name, len(f), fk, wk, rd, wr, rd + wr))
+        rows.append("| %s | %d | %d | %d | %.3f | %.3f | %.3f |" % (cfg.name, nf, fk, wk, rd, wr, rd + wr))
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
