@@ -442,8 +442,8 @@ int enqueue_expert_gemm(moe_handle_t h, const Plan& p, void* ws, bool up, const 
   // their own (two blocks per CU), after the full row tiles
   const bool fp4_rem = wt == WT_NVFP4 && p.bm == 256 && p.bms == 128;
   if (p.bms > 0 && (prof_split() || fp4_rem)) {
-    // with phase-split timing the two lists are two launches of the same
-    // kernel otherwise (same results)
+    // phase-split timing also runs the two lists as two launches, timed apart
+    // (for other weights both on the grouped kernel; same results either way)
     a.lists = 1;
     MOE_TRY(launch_gemm_bf16(a, wt, epi, p.bm, bn, p.bms, items, h->num_cu, s));
     a.lists = 2;
